@@ -1,0 +1,610 @@
+/*
+ * pararnn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU statement of what the ParaRNN hot path computes.
+ * It exists so that the GPU library can be checked against something that a
+ * reader can verify by eye.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.
+ * It shares no code, header or table with the GPU library.
+ *
+ * Sources (the pages are cited by title and section):
+ *  - pararnn-torch README (PyPI page), section "Method": the whole hidden
+ *    trajectory H is the unknown of F(H)_t = h_t - f(h_{t-1}, x_t) = 0, solved
+ *    with Newton updates whose linear solves are associative scans over time.
+ *  - same page, "Method": the backward pass follows the paper's adjoint
+ *    equation (a reverse linear recurrence with transposed Jacobians).
+ *  - ParaRNN abstract (HF paper list): Newton iterations combined with
+ *    parallel reductions, applied to adaptations of LSTM and GRU.
+ *  - The diagonal GRU cell equations are the benchmark statement that comes
+ *    with this code base; the LSTM is the textbook cell without peepholes
+ *    whose recurrent weights are diagonal and act on h (a reading: the pages
+ *    print no LSTM equations).
+ *
+ * Everything is sequential in time and in fp64; std C math (exp, tanh) only.
+ * Threads split the B*D independent channels; each channel walks T serially.
+ *
+ * Parity pins: see tests/test_oracle_*.py.  Every function below is pinned by
+ * a closed form, a brute-force sum, a library routine (torch GRUCell /
+ * LSTMCell, numpy.linalg.solve, autograd) or a finite-difference check.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_LINEAR = 0, OR_GRU = 1, OR_LSTM = 2 };
+enum { OR_OK = 0, OR_EINVAL = -1, OR_ENOMEM = -2, OR_DIVERGED = -5 };
+
+/* ------------------------------------------------------------------------ */
+/* input decoding                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* A bf16 value is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_bits_to_double(uint16_t v) {
+  uint32_t u = (uint32_t)v << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_in(const void* p, int dtype, int64_t i) {
+  if (dtype == OR_BF16) return bf16_bits_to_double(((const uint16_t*)p)[i]);
+  return (double)((const float*)p)[i];
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static int state_size(int cell) { return cell == OR_LSTM ? 2 : 1; }
+static int gate_count(int cell) {
+  return cell == OR_LSTM ? 4 : (cell == OR_GRU ? 3 : 2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* one cell step                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * or_cell_step: s_next = f(s, x) for one channel, with
+ *   J[S*S]     = d s_next / d s        (row-major: J[i*S+j] = d s_next_i / d s_j)
+ *   dfdu[S*G]  = d s_next / d u_g      (dfdu[i*G+g]), u_g the full gate
+ *                pre-activation  u_g = U_g + w_g * (input of w_g) + bias_g
+ *   wcoef[G]   = the factor that multiplies w_g inside u_g
+ * Any of J, dfdu, wcoef may be NULL.
+ *
+ * GRU (state h; gates z, r, c; benchmark statement of the diagonal GRU):
+ *   z = sig(U_z + a_z h + b_z),  r = sig(U_r + a_r h + b_r)
+ *   c = tanh(U_c + a_c (r h) + b_c),  h' = (1 - z) h + z c
+ * LSTM (state (c, h); gates i, f, o, g; textbook cell, diagonal w on h):
+ *   i,f,o = sig(U + w h + b),  g = tanh(U_g + w_g h + b_g)
+ *   c' = f c + i g,  h' = o tanh(c')
+ * LINEAR (state h; "gates" a, b are the coefficients themselves):
+ *   h' = a h + b
+ * u[] for LINEAR holds (a_t, b_t); w and bias are ignored.
+ */
+int or_cell_step(int cell, const double* u_in, const double* w,
+                 const double* bias, const double* s, double* s_next,
+                 double* J, double* dfdu, double* wcoef) {
+  if (cell == OR_LINEAR) {
+    double a = u_in[0], b = u_in[1], h = s[0];
+    s_next[0] = a * h + b;
+    if (J) J[0] = a;
+    if (dfdu) { dfdu[0] = h; dfdu[1] = 1.0; }
+    if (wcoef) { wcoef[0] = 0.0; wcoef[1] = 0.0; }
+    return OR_OK;
+  }
+  if (cell == OR_GRU) {
+    double h = s[0];
+    double z = sigmoid(u_in[0] + w[0] * h + bias[0]);
+    double r = sigmoid(u_in[1] + w[1] * h + bias[1]);
+    double c = tanh(u_in[2] + w[2] * (r * h) + bias[2]);
+    s_next[0] = (1.0 - z) * h + z * c;
+    /* partial derivatives of h' with respect to each gate pre-activation */
+    double d_uz = (c - h) * z * (1.0 - z);           /* via z            */
+    double d_uc = z * (1.0 - c * c);                 /* via c            */
+    double d_ur = d_uc * w[2] * h * r * (1.0 - r);   /* via r inside c   */
+    if (dfdu) { dfdu[0] = d_uz; dfdu[1] = d_ur; dfdu[2] = d_uc; }
+    if (wcoef) { wcoef[0] = h; wcoef[1] = h; wcoef[2] = r * h; }
+    if (J) {
+      /* dh'/dh = (1-z) + (c-h) dz/dh + z dc/dh,
+         dz/dh = z(1-z) a_z,  dc/dh = (1-c^2) a_c (r + h dr/dh),
+         dr/dh = r(1-r) a_r                                            */
+      double dz_dh = z * (1.0 - z) * w[0];
+      double dr_dh = r * (1.0 - r) * w[1];
+      double dc_dh = (1.0 - c * c) * w[2] * (r + h * dr_dh);
+      J[0] = (1.0 - z) + (c - h) * dz_dh + z * dc_dh;
+    }
+    return OR_OK;
+  }
+  if (cell == OR_LSTM) {
+    double c = s[0], h = s[1];
+    double ig = sigmoid(u_in[0] + w[0] * h + bias[0]);
+    double fg = sigmoid(u_in[1] + w[1] * h + bias[1]);
+    double og = sigmoid(u_in[2] + w[2] * h + bias[2]);
+    double gg = tanh(u_in[3] + w[3] * h + bias[3]);
+    double c2 = fg * c + ig * gg;
+    double tc = tanh(c2);
+    double h2 = og * tc;
+    s_next[0] = c2;
+    s_next[1] = h2;
+    /* d c' / d u_gate (gate order i, f, o, g); o does not enter c' */
+    double dc_du[4] = {gg * ig * (1.0 - ig), c * fg * (1.0 - fg), 0.0,
+                       ig * (1.0 - gg * gg)};
+    double kh = og * (1.0 - tc * tc); /* d h' / d c' */
+    double dh_du[4] = {kh * dc_du[0], kh * dc_du[1], tc * og * (1.0 - og),
+                       kh * dc_du[3]};
+    if (dfdu) {
+      for (int g = 0; g < 4; ++g) { dfdu[0 * 4 + g] = dc_du[g]; dfdu[1 * 4 + g] = dh_du[g]; }
+    }
+    if (wcoef) { for (int g = 0; g < 4; ++g) wcoef[g] = h; }
+    if (J) {
+      /* every gate sees h through w_g * h, so d c'/d h = sum_g dc_du[g] w_g */
+      double dc_dh = dc_du[0] * w[0] + dc_du[1] * w[1] + dc_du[3] * w[3];
+      double dh_dh = dh_du[2] * w[2] + kh * dc_dh;
+      J[0] = fg;        /* d c'/d c */
+      J[1] = dc_dh;     /* d c'/d h */
+      J[2] = kh * fg;   /* d h'/d c */
+      J[3] = dh_dh;     /* d h'/d h */
+    }
+    return OR_OK;
+  }
+  return OR_EINVAL;
+}
+
+/* ------------------------------------------------------------------------ */
+/* problem description shared by the entry points below                     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t cell;
+  int32_t dtype;       /* storage of pre[] */
+  int64_t B, T, D;
+  const void* pre[4];  /* G planes [B][T][D] */
+  const float* w;      /* [G][D] (GRU, LSTM)  */
+  const float* bias;   /* [G][D] (GRU, LSTM)  */
+  const float* s0;     /* [S][B][D] or NULL (zeros) */
+} or_problem;
+
+static int64_t elem_index(const or_problem* p, int64_t b, int64_t t, int64_t d) {
+  return (b * p->T + t) * p->D + d;
+}
+
+/* gate inputs of channel (b,d) at time t, decoded to fp64 */
+static void gather_u(const or_problem* p, int64_t b, int64_t t, int64_t d, double* u) {
+  int G = gate_count(p->cell);
+  int64_t i = elem_index(p, b, t, d);
+  for (int g = 0; g < G; ++g) u[g] = load_in(p->pre[g], p->dtype, i);
+}
+
+static void gather_params(const or_problem* p, int64_t d, double* w, double* bias) {
+  int G = gate_count(p->cell);
+  for (int g = 0; g < G; ++g) {
+    w[g] = (p->cell == OR_LINEAR) ? 0.0 : (double)p->w[g * p->D + d];
+    bias[g] = (p->cell == OR_LINEAR) ? 0.0 : (double)p->bias[g * p->D + d];
+  }
+}
+
+static void gather_s0(const or_problem* p, int64_t b, int64_t d, double* s) {
+  int S = state_size(p->cell);
+  for (int k = 0; k < S; ++k)
+    s[k] = p->s0 ? (double)p->s0[(k * p->B + b) * p->D + d] : 0.0;
+}
+
+/* state plane k of a trajectory laid out [S][B][T][D] */
+static int64_t traj_index(const or_problem* p, int k, int64_t b, int64_t t, int64_t d) {
+  return ((k * p->B + b) * p->T + t) * p->D + d;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a tiny thread pool over channels                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*channel_fn)(void* ctx, int64_t ch0, int64_t ch1, int worker);
+
+typedef struct {
+  channel_fn fn;
+  void* ctx;
+  int64_t ch0, ch1;
+  int worker;
+} worker_arg;
+
+static void* worker_main(void* a) {
+  worker_arg* w = (worker_arg*)a;
+  w->fn(w->ctx, w->ch0, w->ch1, w->worker);
+  return NULL;
+}
+
+static int run_channels(int64_t n_channels, int nthreads, channel_fn fn, void* ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n_channels) nthreads = (int)(n_channels > 0 ? n_channels : 1);
+  if (nthreads == 1) { fn(ctx, 0, n_channels, 0); return OR_OK; }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  worker_arg* args = (worker_arg*)malloc(sizeof(worker_arg) * nthreads);
+  if (!th || !args) { free(th); free(args); return OR_ENOMEM; }
+  for (int i = 0; i < nthreads; ++i) {
+    args[i].fn = fn;
+    args[i].ctx = ctx;
+    args[i].ch0 = n_channels * i / nthreads;
+    args[i].ch1 = n_channels * (i + 1) / nthreads;
+    args[i].worker = i;
+    pthread_create(&th[i], NULL, worker_main, &args[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(args);
+  return OR_OK;
+}
+
+static int check_problem(const or_problem* p) {
+  if (!p || p->B < 0 || p->T < 0 || p->D < 0) return OR_EINVAL;
+  if (p->cell != OR_LINEAR && p->cell != OR_GRU && p->cell != OR_LSTM) return OR_EINVAL;
+  if (p->dtype != OR_F32 && p->dtype != OR_BF16) return OR_EINVAL;
+  int G = gate_count(p->cell);
+  for (int g = 0; g < G; ++g)
+    if (!p->pre[g] && p->B * p->T * p->D > 0) return OR_EINVAL;
+  if (p->cell != OR_LINEAR && (!p->w || !p->bias) && p->D > 0) return OR_EINVAL;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* sequential unroll: s_t = f(s_{t-1}, x_t), the exact solution of F(H)=0    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const or_problem* p;
+  double* out;
+} unroll_ctx;
+
+static void unroll_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  (void)worker;
+  unroll_ctx* c = (unroll_ctx*)vctx;
+  const or_problem* p = c->p;
+  int S = state_size(p->cell);
+  double u[4], w[4], bias[4], s[2], sn[2];
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / p->D, d = ch % p->D;
+    gather_params(p, d, w, bias);
+    gather_s0(p, b, d, s);
+    for (int64_t t = 0; t < p->T; ++t) {
+      gather_u(p, b, t, d, u);
+      or_cell_step(p->cell, u, w, bias, s, sn, NULL, NULL, NULL);
+      for (int k = 0; k < S; ++k) {
+        s[k] = sn[k];
+        c->out[traj_index(p, k, b, t, d)] = s[k];
+      }
+    }
+  }
+}
+
+int or_unroll(const or_problem* p, double* out, int nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  unroll_ctx c = {p, out};
+  return run_channels(p->B * p->D, nthreads, unroll_channels, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* residual of a trajectory: max over b,t,d,state of |h_t - f(h_{t-1},x_t)|  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const or_problem* p;
+  const double* H;
+  double* worker_max;
+} resid_ctx;
+
+/* NaN-propagating maximum: a NaN anywhere makes the result NaN */
+static double nan_max(double m, double x) { return (x > m || x != x) ? x : m; }
+
+static void resid_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  resid_ctx* c = (resid_ctx*)vctx;
+  const or_problem* p = c->p;
+  int S = state_size(p->cell);
+  double u[4], w[4], bias[4], prev[2], sn[2], m = 0.0;
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / p->D, d = ch % p->D;
+    gather_params(p, d, w, bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      if (t == 0) gather_s0(p, b, d, prev);
+      else for (int k = 0; k < S; ++k) prev[k] = c->H[traj_index(p, k, b, t - 1, d)];
+      gather_u(p, b, t, d, u);
+      or_cell_step(p->cell, u, w, bias, prev, sn, NULL, NULL, NULL);
+      for (int k = 0; k < S; ++k) m = nan_max(m, fabs(c->H[traj_index(p, k, b, t, d)] - sn[k]));
+    }
+  }
+  c->worker_max[worker] = m;
+}
+
+int or_residual(const or_problem* p, const double* H, double* out_max, int nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (nthreads < 1) nthreads = 1;
+  double* wm = (double*)calloc((size_t)nthreads, sizeof(double));
+  if (!wm) return OR_ENOMEM;
+  resid_ctx c = {p, H, wm};
+  rc = run_channels(p->B * p->D, nthreads, resid_channels, &c);
+  double m = 0.0;
+  for (int i = 0; i < nthreads; ++i) m = nan_max(m, wm[i]);
+  free(wm);
+  *out_max = m;
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Newton on F(H) = 0 (pararnn-torch README, "Method")                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Iteration k, at the current trajectory H^k (H^k_{-1} := s0):
+ *   r_t = h^k_t - f(h^k_{t-1}, x_t)                       (residual)
+ *   J_t = d f / d s  at (h^k_{t-1}, x_t)                  (Jacobian)
+ *   R_k = max |r_t|                                      (max residual)
+ *   delta_{-1} = 0,  delta_t = J_t delta_{t-1} - r_t       (linearised system,
+ *                                                          solved sequentially)
+ *   H^{k+1} = H^k + delta
+ * Stop rule (a reading; the pages give none): with tol <= 0 exactly max_iters
+ * iterations run.  With tol > 0 the iteration whose evaluated residual R_k is
+ * below tol is the last one; its update is still applied (the fused GPU pass
+ * evaluates the residual and produces the update in one sweep).  A
+ * non-finite R_k stops the loop and reports divergence.
+ * Output: H^{iters}; resid[0..iters-1] = R_0..R_{iters-1}.
+ */
+
+typedef struct {
+  const or_problem* p;
+  double* H;          /* in/out trajectory [S][B][T][D] */
+  double* worker_max;
+  double* scratch;    /* per worker: T * (S + S*S + S) doubles */
+} newton_ctx;
+
+static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  newton_ctx* c = (newton_ctx*)vctx;
+  const or_problem* p = c->p;
+  int S = state_size(p->cell);
+  int64_t T = p->T;
+  double* r = c->scratch + (size_t)worker * (size_t)T * (size_t)(2 * S + S * S);
+  double* J = r + T * S;
+  double* delta = J + T * S * S;
+  double u[4], w[4], bias[4], prev[2], sn[2], m = 0.0;
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / p->D, d = ch % p->D;
+    gather_params(p, d, w, bias);
+    /* residual and Jacobian at the current iterate */
+    for (int64_t t = 0; t < T; ++t) {
+      if (t == 0) gather_s0(p, b, d, prev);
+      else for (int k = 0; k < S; ++k) prev[k] = c->H[traj_index(p, k, b, t - 1, d)];
+      gather_u(p, b, t, d, u);
+      or_cell_step(p->cell, u, w, bias, prev, sn, J + t * S * S, NULL, NULL);
+      for (int k = 0; k < S; ++k) {
+        r[t * S + k] = c->H[traj_index(p, k, b, t, d)] - sn[k];
+        m = nan_max(m, fabs(r[t * S + k]));
+      }
+    }
+    /* sequential solve of the linearised recurrence */
+    for (int64_t t = 0; t < T; ++t) {
+      for (int i = 0; i < S; ++i) {
+        double acc = -r[t * S + i];
+        if (t > 0)
+          for (int j = 0; j < S; ++j) acc += J[t * S * S + i * S + j] * delta[(t - 1) * S + j];
+        delta[t * S + i] = acc;
+      }
+    }
+    for (int64_t t = 0; t < T; ++t)
+      for (int k = 0; k < S; ++k) c->H[traj_index(p, k, b, t, d)] += delta[t * S + k];
+  }
+  c->worker_max[worker] = m;
+}
+
+int or_newton(const or_problem* p, const float* init_guess, int max_iters, double tol,
+              double* H, double* resid, int* iters, int* converged, int nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (max_iters < 1) return OR_EINVAL;
+  int S = state_size(p->cell);
+  int64_t n = (int64_t)S * p->B * p->T * p->D;
+  for (int64_t i = 0; i < n; ++i) H[i] = init_guess ? (double)init_guess[i] : 0.0;
+  if (nthreads < 1) nthreads = 1;
+  double* wm = (double*)malloc(sizeof(double) * (size_t)nthreads);
+  double* scratch = (double*)malloc(sizeof(double) * (size_t)nthreads *
+                                    (size_t)(p->T > 0 ? p->T : 1) * (size_t)(2 * S + S * S));
+  if (!wm || !scratch) { free(wm); free(scratch); return OR_ENOMEM; }
+  newton_ctx c = {p, H, wm, scratch};
+  int k_done = 0, conv = 0, status = OR_OK;
+  for (int k = 0; k < max_iters; ++k) {
+    for (int i = 0; i < nthreads; ++i) wm[i] = 0.0;
+    rc = run_channels(p->B * p->D, nthreads, newton_channels, &c);
+    if (rc) { status = rc; break; }
+    double R = 0.0;
+    for (int i = 0; i < nthreads; ++i) R = nan_max(R, wm[i]);
+    resid[k] = R;
+    k_done = k + 1;
+    if (!isfinite(R)) { status = OR_DIVERGED; break; } /* NaN or Inf */
+    if (tol > 0.0 && R < tol) { conv = 1; break; }
+  }
+  free(wm);
+  free(scratch);
+  *iters = k_done;
+  *converged = conv;
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* linear recurrence, S = 1 or 2, forward or reverse                         */
+/* ------------------------------------------------------------------------ */
+/*
+ * forward:  s_{-1} = s0,  s_t = A_t s_{t-1} + b_t,  t = 0..T-1
+ * reverse:  s_T    = s0,  s_t = A_t s_{t+1} + b_t,  t = T-1..0
+ * S = 1: a is [B][T][D], b is [B][T][D].
+ * S = 2: a is [4][B][T][D] (A00, A01, A10, A11 row-major), b is [2][B][T][D].
+ * This is the recurrence that every Newton linear solve reduces to
+ * (pararnn-torch README, "Method": each linear solve is an associative scan);
+ * here it is evaluated by its definition, one step after another.
+ */
+
+typedef struct {
+  int S, dtype, reverse;
+  int64_t B, T, D;
+  const void* a;
+  const void* b;
+  const float* s0;
+  double* out;
+} lin_ctx;
+
+static void lin_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  (void)worker;
+  lin_ctx* c = (lin_ctx*)vctx;
+  int64_t N = c->B * c->T * c->D;
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / c->D, d = ch % c->D;
+    double s[2] = {0.0, 0.0};
+    for (int k = 0; k < c->S; ++k) s[k] = c->s0 ? (double)c->s0[(k * c->B + b) * c->D + d] : 0.0;
+    for (int64_t step = 0; step < c->T; ++step) {
+      int64_t t = c->reverse ? c->T - 1 - step : step;
+      int64_t i = (b * c->T + t) * c->D + d;
+      if (c->S == 1) {
+        s[0] = load_in(c->a, c->dtype, i) * s[0] + load_in(c->b, c->dtype, i);
+        c->out[i] = s[0];
+      } else {
+        double a00 = load_in(c->a, c->dtype, 0 * N + i), a01 = load_in(c->a, c->dtype, 1 * N + i);
+        double a10 = load_in(c->a, c->dtype, 2 * N + i), a11 = load_in(c->a, c->dtype, 3 * N + i);
+        double n0 = a00 * s[0] + a01 * s[1] + load_in(c->b, c->dtype, 0 * N + i);
+        double n1 = a10 * s[0] + a11 * s[1] + load_in(c->b, c->dtype, 1 * N + i);
+        s[0] = n0;
+        s[1] = n1;
+        c->out[0 * N + i] = n0;
+        c->out[1 * N + i] = n1;
+      }
+    }
+  }
+}
+
+int or_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void* a,
+                   const void* b, const float* s0, int reverse, double* out, int nthreads) {
+  if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return OR_EINVAL;
+  if (dtype != OR_F32 && dtype != OR_BF16) return OR_EINVAL;
+  lin_ctx c = {S, dtype, reverse ? 1 : 0, B, T, D, a, b, s0, out};
+  return run_channels(B * D, nthreads, lin_channels, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* VJP at a solved trajectory (README "Method": backward by the adjoint)     */
+/* ------------------------------------------------------------------------ */
+/*
+ * For L with dL/dh_t = g_t given on the h component of the state:
+ *   lambda_{T-1} = e_h g_{T-1}
+ *   lambda_t     = e_h g_t + J_{t+1}^T lambda_{t+1}        (reverse, sequential)
+ *   J_{t+1} = d f/d s at (s_t, x_{t+1})
+ *   dL/du_{gate,t} = sum_i lambda_t[i] * d s_t[i] / d u_gate   at (s_{t-1}, x_t)
+ *   dL/dU_{gate,t} = dL/du_{gate,t}          (U enters u additively)
+ *   dL/dw_gate     = sum_{b,t} dL/du_{gate,t} * (factor of w_gate in u_gate)
+ *   dL/dbias_gate  = sum_{b,t} dL/du_{gate,t}
+ *   dL/ds0         = J_0^T lambda_0,  J_0 = d f/d s at (s0, x_0)
+ * LINEAR: dL/da_t = lambda_t h_{t-1}, dL/db_t = lambda_t, dL/ds0 = a_0 lambda_0.
+ * e_h is the unit vector of h (for the LSTM state (c, h), e_h = (0, 1)).
+ * Sums over (b, t) are accumulated in plain sequential order per channel.
+ */
+
+typedef struct {
+  const or_problem* p;
+  const double* s;    /* trajectory [S][B][T][D] */
+  const float* g;     /* [B][T][D] */
+  double* d_pre;      /* [G][B][T][D] */
+  double* lam;        /* [S][B][T][D] or NULL */
+  double* d_s0;       /* [S][B][D] or NULL */
+  double* wpart;      /* [B*D][G] per-channel sums of dL/dw */
+  double* bpart;      /* [B*D][G] per-channel sums of dL/dbias */
+  double* scratch;    /* per worker: T * S doubles */
+} vjp_ctx;
+
+static void vjp_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  vjp_ctx* c = (vjp_ctx*)vctx;
+  const or_problem* p = c->p;
+  int S = state_size(p->cell), G = gate_count(p->cell);
+  int64_t T = p->T, N = p->B * p->T * p->D;
+  double* lam = c->scratch + (size_t)worker * (size_t)T * (size_t)S;
+  double u[4], w[4], bias[4], prev[2], sn[2], J[4], dfdu[8], wcoef[4];
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / p->D, d = ch % p->D;
+    gather_params(p, d, w, bias);
+    /* adjoint recurrence, backwards in time */
+    for (int64_t t = T - 1; t >= 0; --t) {
+      double acc[2] = {0.0, 0.0};
+      acc[S - 1] = (double)c->g[elem_index(p, b, t, d)]; /* e_h g_t */
+      if (t + 1 < T) {
+        for (int k = 0; k < S; ++k) prev[k] = c->s[traj_index(p, k, b, t, d)];
+        gather_u(p, b, t + 1, d, u);
+        or_cell_step(p->cell, u, w, bias, prev, sn, J, NULL, NULL);
+        for (int i = 0; i < S; ++i)            /* (J^T lambda)_i = sum_j J[j][i] lambda_j */
+          for (int j = 0; j < S; ++j) acc[i] += J[j * S + i] * lam[(t + 1) * S + j];
+      }
+      for (int i = 0; i < S; ++i) lam[t * S + i] = acc[i];
+    }
+    /* gate gradients and parameter sums, forwards in time */
+    double wsum[4] = {0, 0, 0, 0}, bsum[4] = {0, 0, 0, 0};
+    for (int64_t t = 0; t < T; ++t) {
+      if (t == 0) gather_s0(p, b, d, prev);
+      else for (int k = 0; k < S; ++k) prev[k] = c->s[traj_index(p, k, b, t - 1, d)];
+      gather_u(p, b, t, d, u);
+      or_cell_step(p->cell, u, w, bias, prev, sn, J, dfdu, wcoef);
+      for (int gi = 0; gi < G; ++gi) {
+        double du = 0.0;
+        for (int i = 0; i < S; ++i) du += lam[t * S + i] * dfdu[i * G + gi];
+        c->d_pre[gi * N + elem_index(p, b, t, d)] = du;
+        wsum[gi] += du * wcoef[gi];
+        bsum[gi] += du;
+      }
+      if (c->lam)
+        for (int k = 0; k < S; ++k) c->lam[traj_index(p, k, b, t, d)] = lam[t * S + k];
+      if (t == 0 && c->d_s0) {
+        for (int i = 0; i < S; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < S; ++j) acc += J[j * S + i] * lam[0 * S + j];
+          c->d_s0[(i * p->B + b) * p->D + d] = acc;
+        }
+      }
+    }
+    if (T == 0 && c->d_s0)
+      for (int i = 0; i < S; ++i) c->d_s0[(i * p->B + b) * p->D + d] = 0.0;
+    for (int gi = 0; gi < G; ++gi) {
+      c->wpart[ch * G + gi] = wsum[gi];
+      c->bpart[ch * G + gi] = bsum[gi];
+    }
+  }
+}
+
+int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, double* d_w,
+           double* d_bias, double* d_s0, double* lam, int nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  int S = state_size(p->cell), G = gate_count(p->cell);
+  int64_t C = p->B * p->D;
+  if (nthreads < 1) nthreads = 1;
+  double* wpart = (double*)calloc((size_t)(C > 0 ? C : 1) * (size_t)G, sizeof(double));
+  double* bpart = (double*)calloc((size_t)(C > 0 ? C : 1) * (size_t)G, sizeof(double));
+  double* scratch = (double*)malloc(sizeof(double) * (size_t)nthreads *
+                                    (size_t)(p->T > 0 ? p->T : 1) * (size_t)S);
+  if (!wpart || !bpart || !scratch) { free(wpart); free(bpart); free(scratch); return OR_ENOMEM; }
+  vjp_ctx c = {p, s, g, d_pre, lam, d_s0, wpart, bpart, scratch};
+  rc = run_channels(C, nthreads, vjp_channels, &c);
+  /* parameter gradients: sum over batch of the per-channel sums (b ascending) */
+  if (rc == OR_OK && p->cell != OR_LINEAR) {
+    for (int gi = 0; gi < G; ++gi) {
+      for (int64_t d = 0; d < p->D; ++d) {
+        double ws = 0.0, bs = 0.0;
+        for (int64_t b = 0; b < p->B; ++b) {
+          ws += wpart[(b * p->D + d) * G + gi];
+          bs += bpart[(b * p->D + d) * G + gi];
+        }
+        if (d_w) d_w[gi * p->D + d] = ws;
+        if (d_bias) d_bias[gi * p->D + d] = bs;
+      }
+    }
+  }
+  free(wpart);
+  free(bpart);
+  free(scratch);
+  return rc;
+}
+
+/* ABI version of this file's entry points, so the wrapper can check it */
+int or_abi_version(void) { return 3; }

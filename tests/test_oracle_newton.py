@@ -1,0 +1,166 @@
+"""Pins for the oracle's Newton solve of F(H)_t = h_t - f(h_{t-1}, x_t) = 0.
+
+Method (pararnn-torch README, "Method"; ParaRNN abstract, HF paper list): the
+whole trajectory H is the unknown; each Newton update solves the linearised
+system, which for a recurrence is lower block-bidiagonal, by a scan over time.
+The oracle solves that system sequentially.  These tests pin it to
+  * dense Newton on the full system: F built from the torch library cells,
+    its Jacobian by torch autograd, each step solved with numpy.linalg.solve;
+  * triangular exactness: after k updates from any guess the first k steps
+    equal the sequential unroll (causality of F);
+  * special cases that are exact after a known number of updates
+    (linear cell: 1; GRU without recurrent weights: 1; LSTM without
+    recurrent weights: 2, not 1);
+  * monotone decrease of the max residual on the benchmark distributions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nonlinear_rnn_solve_amd import synth
+from test_oracle_cells import torch_gru_cell, torch_lstm_cell
+
+torch.set_default_dtype(torch.float64)
+
+
+def dense_F(inp, s0):
+    """F(H)_t = s_t - f(s_{t-1}, x_t) on the flattened trajectory, built from the torch library cells."""
+    B, T, D, S = inp.B, inp.T, inp.D, inp.S
+    pre = [torch.tensor(p.astype(np.float64)) for p in inp.pre_f32()]
+    s0t = torch.tensor(s0.astype(np.float64))
+    if inp.cell == "linear":
+        cell = lambda x, h: x[:, :D] * h + x[:, D:]   # noqa: E731  (h' = a h + b)
+    else:
+        w, bias = inp.w.astype(np.float64), inp.bias.astype(np.float64)
+        cell = torch_gru_cell(w, bias) if inp.cell == "gru" else torch_lstm_cell(w, bias)
+
+    def F(flat):
+        H = flat.reshape(S, B, T, D)
+        out = []
+        for t in range(T):
+            prev = s0t if t == 0 else H[:, :, t - 1, :]
+            x = torch.cat([p[:, t, :] for p in pre], 1)
+            if S == 1:
+                f = cell(x, prev[0])[None]
+            else:
+                h2, c2 = cell(x, (prev[1], prev[0]))
+                f = torch.stack([c2, h2])
+            out.append(H[:, :, t, :] - f)
+        return torch.stack(out, 2).reshape(-1)
+    return F
+
+
+def dense_newton(inp, s0, K):
+    """Newton on the stacked system with an explicit Jacobian; returns the K-th iterate [S][B][T][D]."""
+    S, B, T, D = inp.S, inp.B, inp.T, inp.D
+    F = dense_F(inp, s0)
+    H = torch.zeros(S * B * T * D)
+    for _ in range(K):
+        Jf = torch.autograd.functional.jacobian(F, H).numpy()
+        step = np.linalg.solve(Jf, F(H).detach().numpy())
+        H = H - torch.tensor(step)
+    return H.reshape(S, B, T, D).numpy()
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_iterates_match_dense_newton(cell, K):
+    inp = synth.make_inputs(cell, 1, 7, 2, seed=1005)
+    s0 = synth.random_state(inp.S, 1, 2, seed=3)
+    prob = oracle.Problem(cell, inp.pre, inp.w, inp.bias, s0=s0)
+    H, res, iters, conv, rc = oracle.newton(prob, K)
+    assert iters == K and rc == oracle.OK
+    np.testing.assert_allclose(H, dense_newton(inp, s0, K), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_triangular_exactness(cell):
+    inp = synth.make_inputs(cell, 2, 12, 3, seed=1006)
+    prob = oracle.Problem(cell, inp.pre, inp.w, inp.bias)
+    ref = oracle.unroll(prob)
+    for k in (1, 3, 7):
+        H = oracle.newton(prob, k)[0]
+        np.testing.assert_allclose(H[:, :, :k, :], ref[:, :, :k, :], atol=1e-13)
+        if k == 1:
+            assert np.abs(H[:, :, k:, :] - ref[:, :, k:, :]).max() > 1e-6   # not yet exact further on
+    H = oracle.newton(prob, 12)[0]
+    np.testing.assert_allclose(H, ref, atol=1e-13)
+
+
+def test_triangular_exactness_from_a_random_guess():
+    inp = synth.make_inputs("gru", 1, 10, 4, seed=1007)
+    prob = oracle.Problem("gru", inp.pre, inp.w, inp.bias)
+    guess = np.random.default_rng(1).standard_normal((1, 1, 10, 4)).astype(np.float32)
+    ref = oracle.unroll(prob)
+    H = oracle.newton(prob, 4, init_guess=guess)[0]
+    np.testing.assert_allclose(H[:, :, :4], ref[:, :, :4], atol=1e-13)
+
+
+def test_linear_cell_exact_after_one_update():
+    inp = synth.make_inputs("linear", 2, 300, 5, seed=1008)
+    s0 = synth.random_state(1, 2, 5, seed=4)
+    prob = oracle.Problem("linear", inp.pre, s0=s0)
+    H, res, iters, conv, rc = oracle.newton(prob, 2)
+    np.testing.assert_allclose(H[0], oracle.linear_scan(*inp.pre, s0=s0), atol=1e-12)
+    assert res[1] < 1e-12 * max(1.0, np.abs(H).max())   # a second update finds nothing to correct
+
+
+def test_gru_without_recurrent_weights_exact_after_one():
+    inp = synth.make_inputs("gru", 1, 64, 4, seed=1009)
+    prob = oracle.Problem("gru", inp.pre, np.zeros_like(inp.w), inp.bias)
+    H = oracle.newton(prob, 1)[0]
+    np.testing.assert_allclose(H, oracle.unroll(prob), atol=1e-13)
+
+
+def test_lstm_without_recurrent_weights_exact_after_two_not_one():
+    inp = synth.make_inputs("lstm", 1, 64, 4, seed=1010)
+    prob = oracle.Problem("lstm", inp.pre, np.zeros_like(inp.w), inp.bias)
+    ref = oracle.unroll(prob)
+    H1 = oracle.newton(prob, 1)[0]
+    np.testing.assert_allclose(H1[0], ref[0], atol=1e-13)          # c is a linear recurrence in c
+    assert np.abs(H1[1] - ref[1]).max() > 1e-3                      # h is not yet right
+    np.testing.assert_allclose(oracle.newton(prob, 2)[0], ref, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(1000, 1010))
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_residuals_decrease_monotonically(cell, seed):
+    inp = synth.make_inputs(cell, 1, 512, 16, seed=seed)
+    prob = oracle.Problem(cell, inp.pre, inp.w, inp.bias)
+    H, res, iters, conv, rc = oracle.newton(prob, 6)
+    assert np.all(np.diff(res) < 0), res
+    # the recorded history is the residual of each iterate fed to the update
+    np.testing.assert_allclose(res[-1], oracle.residual(prob, oracle.newton(prob, 5)[0]), rtol=1e-12)
+    assert oracle.residual(prob, H) < 1e-10
+
+
+def test_tolerance_stop_rule():
+    inp = synth.make_inputs("gru", 1, 256, 8, seed=1011)
+    prob = oracle.Problem("gru", inp.pre, inp.w, inp.bias)
+    _, full, _, _, _ = oracle.newton(prob, 8)
+    tol = 1e-5
+    H, res, iters, conv, rc = oracle.newton(prob, 8, tol=tol)
+    first_below = int(np.argmax(full < tol))
+    assert conv and rc == oracle.OK
+    assert iters == first_below + 1                  # the update of that iteration is applied
+    np.testing.assert_array_equal(res, full[:iters])
+    np.testing.assert_array_equal(H, oracle.newton(prob, iters)[0])
+    # unreachable tolerance: runs the budget, not converged
+    _, res2, it2, conv2, rc2 = oracle.newton(prob, 2, tol=1e-30)
+    assert it2 == 2 and not conv2 and rc2 == oracle.OK
+
+
+def test_nan_input_reports_divergence():
+    inp = synth.make_inputs("gru", 1, 32, 4, seed=1012)
+    inp.pre[0][0, 5, 2] = np.nan
+    prob = oracle.Problem("gru", inp.pre, inp.w, inp.bias)
+    H, res, iters, conv, rc = oracle.newton(prob, 5, tol=1e-5)
+    assert rc == oracle.DIVERGED and iters == 1 and np.isnan(res[0])
+
+
+def test_residual_of_unroll_is_rounding_level():
+    inp = synth.make_inputs("lstm", 2, 100, 3, seed=1013)
+    prob = oracle.Problem("lstm", inp.pre, inp.w, inp.bias)
+    assert oracle.residual(prob, oracle.unroll(prob)) == 0.0
+    assert oracle.residual(prob, np.zeros(prob.traj_shape())) > 0.1
