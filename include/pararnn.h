@@ -1,0 +1,159 @@
+/*
+ * pararnn.h -- C ABI of libpararnn.so, the MI355X (gfx950) hot path of the
+ * ParaRNN method: Newton solves of diagonal GRU / LSTM recurrences whose
+ * linear solves are parallel scans over time, and the reverse-scan VJP.
+ *
+ * Method (pararnn-torch README on PyPI, section "Method"; ParaRNN abstract on
+ * the HF paper list): the whole hidden trajectory H = (h_0 .. h_{T-1}) is the
+ * unknown of the system  F(H)_t = h_t - f(h_{t-1}, x_t) = 0,  solved with a
+ * few Newton iterations; each iteration's linearised system
+ *     delta_t = J_t delta_{t-1} - r_t,   r_t = h_t - f(h_{t-1}, x_t),
+ *     J_t = d f / d h (h_{t-1}, x_t)
+ * is a first-order linear recurrence and is solved by an associative scan
+ * over time.  The backward pass (same page, "Method") is the adjoint: a
+ * reverse linear recurrence with transposed Jacobians.
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory; the library never allocates device memory and keeps no state
+ *    between calls except a process-wide launch counter.
+ *  - Layouts are dense and row-major: a "[B][T][D]" plane has element
+ *    (b, t, d) at offset (b*T + t)*D + d, channels (d) fastest.  A state
+ *    trajectory "[S][B][T][D]" holds S such planes (LSTM: plane 0 = c,
+ *    plane 1 = h).  Weights and biases are "[G][D]" (gate-major).
+ *  - Every call validates its arguments before launching anything and
+ *    returns a status; nothing throws across the ABI.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Outputs are valid once the stream has completed.  Only a
+ *    non-NULL report makes pararnn_newton_solve wait for the stream.
+ *  - `ws` is a device workspace of at least the queried size, 256-byte
+ *    aligned, whose contents need not be initialised.  Calls that overlap in
+ *    time must use distinct workspaces.
+ *  - Arithmetic is fp32 throughout; bf16 is a storage format for the gate
+ *    pre-activations only.
+ */
+#ifndef PARARNN_H
+#define PARARNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARARNN_ABI_VERSION 1
+/* upper bound of Newton iterations per call (report.residual holds one more) */
+#define PARARNN_MAX_ITERS 64
+
+typedef enum {
+  PARARNN_OK = 0,
+  PARARNN_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum, K outside [1, 64], misalignment */
+  PARARNN_ERR_UNSUPPORTED = -2,  /* valid but not built: D not a multiple of 2, or too large a grid */
+  PARARNN_ERR_WORKSPACE = -3,    /* ws NULL/misaligned or ws_bytes below the queried size */
+  PARARNN_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  PARARNN_ERR_DIVERGED = -5      /* tolerance mode saw a non-finite max residual (report still filled) */
+} pararnn_status;
+
+typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
+
+/* Cells.  G = gate planes, S = state size.
+ *  LINEAR    G=2 (a, b), S=1:  h' = a_t h + b_t  (the pre-activation planes ARE the coefficients)
+ *  DIAG_GRU  G=3 (z, r, c), S=1, diagonal recurrent weights (a_z, a_r, a_c), biases (b_z, b_r, b_c):
+ *              z = sig(U_z + a_z h + b_z),  r = sig(U_r + a_r h + b_r),
+ *              c = tanh(U_c + a_c (r h) + b_c),  h' = (1 - z) h + z c
+ *  DIAG_LSTM G=4 (i, f, o, g), S=2 with state (c, h), diagonal recurrent weights acting on h:
+ *              i, f, o = sig(U + w h + b),  g = tanh(U_g + w_g h + b_g),
+ *              c' = f c + i g,  h' = o tanh(c')                                            */
+typedef enum { PARARNN_CELL_LINEAR = 0, PARARNN_CELL_DIAG_GRU = 1, PARARNN_CELL_DIAG_LSTM = 2 } pararnn_cell;
+
+typedef struct {
+  int32_t cell;          /* pararnn_cell */
+  int32_t pre_dtype;     /* pararnn_dtype of pre[] */
+  int64_t B, T, D;       /* batch, time steps, channels; each >= 0 (an empty problem is a no-op);
+                            D must be even                                                     */
+  const void* pre[4];    /* G gate pre-activation planes [B][T][D], caller-precomputed
+                            (x_t already projected); 8-byte aligned                            */
+  const float* w;        /* [G][D] diagonal recurrent weights (ignored for LINEAR)             */
+  const float* bias;     /* [G][D] biases (ignored for LINEAR)                                 */
+  const float* s0;       /* [S][B][D] initial state h_{-1}; NULL = zeros                        */
+} pararnn_problem;
+
+typedef struct {
+  int32_t max_iters;       /* Newton budget K, 1..PARARNN_MAX_ITERS                                 */
+  float tol;               /* <= 0: run exactly max_iters iterations.
+                              > 0: iteration k evaluates R_k = max|r(H^k)| over b, t, d and state
+                              components; the first iteration with R_k < tol is the last one (its
+                              update is applied).  A non-finite R_k stops the solve (DIVERGED).     */
+  const float* init_guess; /* [S][B][T][D] first iterate H^0, or NULL for H^0 = 0.  May equal s_out
+                              (resume from a previous solve's output).                              */
+  int32_t final_residual;  /* nonzero: one extra pass computes max|r| of the returned trajectory   */
+} pararnn_newton_opts;
+
+typedef struct {          /* (host) */
+  int32_t iters;          /* Newton updates applied (kernels that did work)                          */
+  int32_t converged;      /* tolerance mode: 1 if some R_k < tol; fixed mode: 0                      */
+  int32_t n_residual;     /* entries of residual[] that are set                                      */
+  float residual[PARARNN_MAX_ITERS + 1]; /* R_0 .. R_{iters-1}; then, if final_residual was asked,
+                                            the max residual of the returned trajectory            */
+} pararnn_report;
+
+/* ------------------------------------------------------------------------------------------------
+ * pararnn_newton_solve -- Newton solve of F(H) = 0 for the given cell (pararnn-torch README,
+ * "Method"; ParaRNN abstract).  Each iteration is ONE fused kernel: it evaluates the residual and
+ * the per-channel Jacobian (scalar for GRU, 2x2 for LSTM) at the current iterate, forms the affine
+ * scan elements of the linearised recurrence in registers, combines them across the workgroup and
+ * across time chunks (decoupled look-back), and writes H^{k+1} = H^k + delta in place into s_out.
+ *   s_out  [S][B][T][D] fp32 output trajectory (H^{iters}).  Must not overlap pre/w/bias/s0.
+ *   report (host, nullable): when given, the call waits for the stream and fills it.
+ * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE before any launch; HIP after a failed launch;
+ * DIVERGED (tolerance mode, report given) when a max residual is NaN or Inf.
+ * ---------------------------------------------------------------------------------------------- */
+size_t pararnn_newton_workspace_bytes(const pararnn_problem* prob, const pararnn_newton_opts* opts);
+pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_newton_opts* opts,
+                                    float* s_out, void* ws, size_t ws_bytes, void* stream,
+                                    pararnn_report* report);
+
+/* ------------------------------------------------------------------------------------------------
+ * pararnn_linear_scan -- the linear recurrence every Newton step reduces to (pararnn-torch README,
+ * "Method": each linear solve is an associative scan over time), as a single-pass parallel scan.
+ *   forward (reverse = 0): s_{-1} = s0,  s_t = A_t s_{t-1} + b_t,  t = 0 .. T-1
+ *   reverse (reverse = 1): s_T    = s0,  s_t = A_t s_{t+1} + b_t,  t = T-1 .. 0
+ *   S = 1: a [B][T][D], b [B][T][D];  S = 2: a [4][B][T][D] (A00, A01, A10, A11), b [2][B][T][D].
+ *   dtype: storage of a and b (fp32 or bf16).  s0 [S][B][D] fp32 or NULL (zeros).
+ *   s_out [S][B][T][D] fp32; it may alias a or b exactly (fp32 storage), not partially.
+ * ---------------------------------------------------------------------------------------------- */
+size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D);
+pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype,
+                                   const void* a, const void* b, const float* s0, float* s_out,
+                                   int reverse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * pararnn_scan_vjp -- gradients at a solved trajectory by the adjoint (pararnn-torch README,
+ * "Method": backward follows the paper's adjoint equation).  With dL/dh_t = g_t on the h component:
+ *   lambda_{T-1} = e_h g_{T-1},  lambda_t = e_h g_t + J_{t+1}^T lambda_{t+1}   (one reverse scan)
+ *   dL/dU_{gate,t} = lambda_t . d f / d u_gate (s_{t-1}, x_t)
+ *   dL/dw_gate = sum_{b,t} dL/dU_{gate,t} * (factor of w_gate in u_gate),  dL/dbias = sum dL/dU
+ *   dL/ds0 = J_0^T lambda_0
+ * LINEAR: d_pre = (dL/da_t = lambda_t h_{t-1}, dL/db_t = lambda_t).  Parameter sums are reduced in a
+ * fixed order (bitwise reproducible run to run).
+ *   s          [S][B][T][D] fp32 the trajectory the gradient is taken at (normally a solve's output)
+ *   g          [B][T][D] fp32 upstream gradient on h
+ *   d_pre      [G][B][T][D] fp32 (required)
+ *   d_w, d_bias [G][D] fp32 or NULL (ignored for LINEAR)
+ *   d_s0       [S][B][D] fp32 or NULL;  lambda_out [S][B][T][D] fp32 or NULL
+ * ---------------------------------------------------------------------------------------------- */
+size_t pararnn_vjp_workspace_bytes(const pararnn_problem* prob);
+pararnn_status pararnn_scan_vjp(const pararnn_problem* prob, const float* s, const float* g,
+                                float* d_pre, float* d_w, float* d_bias, float* d_s0,
+                                float* lambda_out, void* ws, size_t ws_bytes, void* stream);
+
+/* human-readable text of a status (static storage) */
+const char* pararnn_status_string(int status);
+/* PARARNN_ABI_VERSION of the built library */
+int pararnn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PARARNN_H */

@@ -1,0 +1,284 @@
+"""Thin Python binding over libpararnn.so (C ABI in include/pararnn.h).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback -- if the library or a GPU is missing, calls raise.
+
+Method references (pararnn-torch README on PyPI, "Method"; ParaRNN abstract):
+Newton on F(H)_t = h_t - f(h_{t-1}, x_t) = 0 with scan-based linear solves, and
+the adjoint (reverse scan) for gradients.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpararnn.so")
+
+CELLS = {"linear": 0, "gru": 1, "lstm": 2}
+GATES = {0: 2, 1: 3, 2: 4}
+STATE = {0: 1, 1: 1, 2: 2}
+MAX_ITERS = 64
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
+          -5: "Newton diverged"}
+
+
+class PararnnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, STATUS.get(status, "?"), status))
+        self.status = status
+
+
+class NewtonDivergenceError(PararnnError):
+    """Raised when a tolerance-mode solve sees a non-finite max residual; carries the history."""
+
+    def __init__(self, status, what, report):
+        super().__init__(status, what)
+        self.report = report
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("cell", ctypes.c_int32), ("pre_dtype", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("pre", ctypes.c_void_p * 4), ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("s0", ctypes.c_void_p)]
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("init_guess", ctypes.c_void_p),
+                ("final_residual", ctypes.c_int32)]
+
+
+class _Report(ctypes.Structure):
+    _fields_ = [("iters", ctypes.c_int32), ("converged", ctypes.c_int32), ("n_residual", ctypes.c_int32),
+                ("residual", ctypes.c_float * (MAX_ITERS + 1))]
+
+
+@dataclass
+class NewtonReport:
+    iters: int
+    converged: bool
+    residuals: list = field(default_factory=list)   # R_0 .. R_{iters-1} (+ final residual if asked)
+    final_residual: float | None = None
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpararnn.so (built by ``python -m nonlinear_rnn_solve_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libpararnn.so not built: run `python -m nonlinear_rnn_solve_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.pararnn_abi_version.restype = i32
+    lib.pararnn_status_string.restype = ctypes.c_char_p
+    lib.pararnn_status_string.argtypes = [i32]
+    lib.pararnn_newton_workspace_bytes.restype = sz
+    lib.pararnn_newton_workspace_bytes.argtypes = [vp, vp]
+    lib.pararnn_newton_solve.restype = i32
+    lib.pararnn_newton_solve.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    lib.pararnn_scan_workspace_bytes.restype = sz
+    lib.pararnn_scan_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.pararnn_linear_scan.restype = i32
+    lib.pararnn_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.pararnn_vjp_workspace_bytes.restype = sz
+    lib.pararnn_vjp_workspace_bytes.argtypes = [vp]
+    lib.pararnn_scan_vjp.restype = i32
+    lib.pararnn_scan_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    if lib.pararnn_abi_version() != 1:
+        raise RuntimeError("libpararnn.so ABI mismatch")
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (no CPU path exists)" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, key: str):
+    """A cached device workspace per (device, key); grown on demand, 256-byte aligned by torch."""
+    k = (str(device), key)
+    buf = _ws_cache.get(k)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[k] = buf
+    return buf
+
+
+def _problem(cell, pre, w, bias, s0):
+    c = CELLS[cell] if isinstance(cell, str) else int(cell)
+    G, S = GATES[c], STATE[c]
+    if len(pre) != G:
+        raise ValueError("cell needs %d pre-activation planes, got %d" % (G, len(pre)))
+    dt = pre[0].dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("pre-activations must be float32 or bfloat16")
+    for i, p in enumerate(pre):
+        _check_dev(p, "pre[%d]" % i, dt)
+        if p.shape != pre[0].shape or p.dim() != 3:
+            raise ValueError("pre planes must all be [B, T, D]")
+    B, T, D = pre[0].shape
+    if c != 0:
+        _check_dev(w, "w", torch.float32)
+        _check_dev(bias, "bias", torch.float32)
+        if tuple(w.shape) != (G, D) or tuple(bias.shape) != (G, D):
+            raise ValueError("w and bias must be [G, D] = [%d, %d]" % (G, D))
+    _check_dev(s0, "s0", torch.float32)
+    if s0 is not None and tuple(s0.shape) != (S, B, D):
+        raise ValueError("s0 must be [S, B, D] = [%d, %d, %d]" % (S, B, D))
+    st = _Problem()
+    st.cell, st.pre_dtype, st.B, st.T, st.D = c, 1 if dt == torch.bfloat16 else 0, B, T, D
+    for i in range(4):
+        st.pre[i] = pre[i].data_ptr() if i < G else None
+    st.w = w.data_ptr() if (c != 0 and w is not None) else None
+    st.bias = bias.data_ptr() if (c != 0 and bias is not None) else None
+    st.s0 = s0.data_ptr() if s0 is not None else None
+    return st, c, G, S, (B, T, D)
+
+
+def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
+    st, *_ = _problem(cell, pre, w, bias, s0)
+    return int(load_library().pararnn_newton_workspace_bytes(ctypes.byref(st), None))
+
+
+def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
+                 final_residual=False, report=True):
+    """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
+
+    pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
+    tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
+    (evaluated at its input iterate) is below tol.  report=True waits for the stream.
+    """
+    lib = load_library()
+    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0)
+    dev = pre[0].device
+    if out is None:
+        out = torch.empty((S, B, T, D), dtype=torch.float32, device=dev)
+    _check_dev(out, "out", torch.float32)
+    _check_dev(init_guess, "init_guess", torch.float32)
+    if tuple(out.shape) != (S, B, T, D):
+        raise ValueError("out must be [S, B, T, D]")
+    if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
+        raise ValueError("init_guess must be [S, B, T, D]")
+    opts = _Opts(int(max_iters), float(tol), init_guess.data_ptr() if init_guess is not None else None,
+                 1 if final_residual else 0)
+    nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
+    ws = _workspace(nbytes, dev, "newton")
+    rep = _Report() if report else None
+    rc = lib.pararnn_newton_solve(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
+                                  _stream(dev), ctypes.byref(rep) if rep is not None else None)
+    r = None
+    if rep is not None:
+        res = [float(rep.residual[i]) for i in range(rep.n_residual)]
+        r = NewtonReport(int(rep.iters), bool(rep.converged), res,
+                         res[rep.iters] if final_residual and rep.n_residual > rep.iters else None)
+    if rc == -5:
+        raise NewtonDivergenceError(rc, "pararnn_newton_solve", r)
+    if rc != 0:
+        raise PararnnError(rc, "pararnn_newton_solve")
+    return out, r
+
+
+def scan_workspace_bytes(S, B, T, D) -> int:
+    return int(load_library().pararnn_scan_workspace_bytes(S, B, T, D))
+
+
+def linear_scan(a, b, s0=None, reverse=False, out=None):
+    """Single-pass parallel linear recurrence.
+
+    S=1: a, b [B, T, D];  S=2: a [4, B, T, D] (A00, A01, A10, A11), b [2, B, T, D].
+    forward: s_t = A_t s_{t-1} + b_t (s_{-1} = s0);  reverse: s_t = A_t s_{t+1} + b_t (s_T = s0).
+    Returns float32 [B, T, D] (S=1) or [2, B, T, D] (S=2).
+    """
+    lib = load_library()
+    S = 2 if a.dim() == 4 else 1
+    _check_dev(a, "a")
+    _check_dev(b, "b", a.dtype)
+    if a.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("a, b must be float32 or bfloat16")
+    B, T, D = b.shape[-3:]
+    if S == 2 and (tuple(a.shape) != (4, B, T, D) or tuple(b.shape) != (2, B, T, D)):
+        raise ValueError("S=2 needs a [4,B,T,D] and b [2,B,T,D]")
+    if S == 1 and tuple(a.shape) != (B, T, D):
+        raise ValueError("a and b must have the same [B,T,D] shape")
+    _check_dev(s0, "s0", torch.float32)
+    if s0 is not None and s0.numel() != S * B * D:
+        raise ValueError("s0 must hold S*B*D values")
+    if out is None:
+        out = torch.empty(b.shape, dtype=torch.float32, device=a.device)
+    _check_dev(out, "out", torch.float32)
+    if out.shape != b.shape:
+        raise ValueError("out must have b's shape")
+    nbytes = lib.pararnn_scan_workspace_bytes(S, B, T, D)
+    ws = _workspace(nbytes, a.device, "scan")
+    rc = lib.pararnn_linear_scan(S, B, T, D, 1 if a.dtype == torch.bfloat16 else 0, _ptr(a), _ptr(b), _ptr(s0),
+                                 _ptr(out), 1 if reverse else 0, _ptr(ws), ws.numel(), _stream(a.device))
+    if rc != 0:
+        raise PararnnError(rc, "pararnn_linear_scan")
+    return out
+
+
+def vjp_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
+    st, *_ = _problem(cell, pre, w, bias, s0)
+    return int(load_library().pararnn_vjp_workspace_bytes(ctypes.byref(st)))
+
+
+def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, want_params=True, want_s0=True):
+    """Gradients at trajectory s ([S,B,T,D] float32) for upstream g = dL/dh ([B,T,D] float32).
+
+    Returns dict: d_pre [G,B,T,D]; d_w, d_bias [G,D] (gated cells); d_s0 [S,B,D]; lam [S,B,T,D] if asked.
+    """
+    lib = load_library()
+    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0)
+    dev = pre[0].device
+    _check_dev(s, "s", torch.float32)
+    _check_dev(g, "g", torch.float32)
+    if tuple(s.shape) != (S, B, T, D) or tuple(g.shape) != (B, T, D):
+        raise ValueError("s must be [S,B,T,D] and g [B,T,D]")
+    d_pre = torch.empty((G, B, T, D), dtype=torch.float32, device=dev)
+    d_w = torch.empty((G, D), dtype=torch.float32, device=dev) if (c != 0 and want_params) else None
+    d_b = torch.empty((G, D), dtype=torch.float32, device=dev) if (c != 0 and want_params) else None
+    d_s0 = torch.empty((S, B, D), dtype=torch.float32, device=dev) if want_s0 else None
+    lam = torch.empty((S, B, T, D), dtype=torch.float32, device=dev) if want_lambda else None
+    nbytes = lib.pararnn_vjp_workspace_bytes(ctypes.byref(st))
+    ws = _workspace(nbytes, dev, "vjp")
+    rc = lib.pararnn_scan_vjp(ctypes.byref(st), _ptr(s), _ptr(g), _ptr(d_pre), _ptr(d_w), _ptr(d_b), _ptr(d_s0),
+                              _ptr(lam), _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise PararnnError(rc, "pararnn_scan_vjp")
+    out = {"d_pre": d_pre, "d_s0": d_s0, "lam": lam}
+    if c != 0 and want_params:
+        out["d_w"], out["d_bias"] = d_w, d_b
+    return out

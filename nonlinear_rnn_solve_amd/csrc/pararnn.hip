@@ -1,0 +1,1483 @@
+// pararnn.hip -- gfx950 (MI355X) kernels and C ABI of libpararnn.so.
+//
+// The ParaRNN hot path (pararnn-torch README on PyPI, section "Method"; ParaRNN
+// abstract on the HF paper list): the trajectory H of a nonlinear recurrence
+// h_t = f(h_{t-1}, x_t) is the unknown of F(H)_t = h_t - f(h_{t-1}, x_t) = 0;
+// Newton iterations solve it, and each iteration's linearised system is a
+// first-order linear recurrence solved by an associative scan over time.  The
+// backward pass is the adjoint: a reverse scan with transposed Jacobians.
+//
+// Design (MI355X first):
+//  * Channels (b, d) are independent for diagonal cells.  A workgroup tile is
+//    TW = 64*V consecutive channels (lane = V channels, loads of 4..16 bytes
+//    per lane, a wave reads one contiguous row) by CT = NW*L time steps (wave
+//    w owns steps [w*L, (w+1)*L) of the chunk, each lane walks its L steps
+//    serially in registers).  No MFMA: nothing here is a dense contraction;
+//    the work is bound by HBM bandwidth.
+//  * One kernel per scan / Newton iteration / VJP.  Each tile (1) produces its
+//    affine scan elements in registers (loaded, or computed from the cell's
+//    residual and Jacobian), (2) reduces them per lane and across waves
+//    through LDS, (3) obtains the state entering its chunk by a decoupled
+//    look-back over the tiles before it in scan order, (4) re-walks its
+//    elements from that state and writes the result.  Inputs are read once.
+//  * The look-back exchanges 64-bit words (32-bit launch tag | fp32 value):
+//    a word is valid when its tag matches the launch, so no flags, fences or
+//    cache maintenance are needed; words are relaxed agent-scope atomics.
+//    Tiles take their position from an atomic ticket, so every tile a tile
+//    waits on is already running (forward progress without co-residency).
+//  * Newton iterations update the trajectory in place; the one value a tile
+//    needs from its predecessor's chunk (h_{t0-1}) travels as a look-back word.
+//
+// Compile with -Xclang -target-feature -Xclang -packed-fp32-ops (no packed
+// fp32 instructions are generated).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "pararnn.h"
+
+#define DEV __device__ __forceinline__
+
+namespace pr {
+
+constexpr int WAVE = 64;
+enum { CELL_LINEAR = 0, CELL_GRU = 1, CELL_LSTM = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// ------------------------------------------------------------------------------------------------
+// device math: exp and reciprocal from the hardware transcendental unit (v_exp_f32 is 2^x,
+// v_rcp_f32 is 1/x, each about 1 ulp); sigmoid and tanh from their definitions.
+// ------------------------------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+DEV float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+DEV float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+DEV float sigmoid(float x) { return hw_rcp(1.0f + hw_exp2(-kLog2e * x)); }
+// tanh(x) = 1 - 2 / (1 + e^{2x})
+DEV float tanh_(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(2.0f * kLog2e * x)), 1.0f); }
+// maximum that lets a NaN win, so a NaN residual is never hidden
+DEV float nanmax(float m, float x) { return (x > m || x != x) ? x : m; }
+
+// ------------------------------------------------------------------------------------------------
+// vector loads / stores of V consecutive channels
+// ------------------------------------------------------------------------------------------------
+template <int V, int DT>
+DEV void ldv(const void* base, int64_t idx, float (&o)[V]) {
+  if constexpr (DT == DT_F32) {
+    const float* p = static_cast<const float*>(base) + idx;
+    if constexpr (V == 1) {
+      o[0] = p[0];
+    } else if constexpr (V == 2) {
+      float2 t = *reinterpret_cast<const float2*>(p);
+      o[0] = t.x; o[1] = t.y;
+    } else {
+      float4 t = *reinterpret_cast<const float4*>(p);
+      o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
+    }
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(static_cast<uint32_t>(p[0]) << 16);
+    } else if constexpr (V == 2) {
+      uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+      o[0] = __uint_as_float(t << 16); o[1] = __uint_as_float(t & 0xffff0000u);
+    } else {
+      uint2 t = *reinterpret_cast<const uint2*>(p);
+      o[0] = __uint_as_float(t.x << 16); o[1] = __uint_as_float(t.x & 0xffff0000u);
+      o[2] = __uint_as_float(t.y << 16); o[3] = __uint_as_float(t.y & 0xffff0000u);
+    }
+  }
+}
+
+template <int V>
+DEV void stv(float* p, const float (&x)[V]) {
+  if constexpr (V == 1) {
+    p[0] = x[0];
+  } else if constexpr (V == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// affine maps x -> A x + b on the S-dimensional state (Blelloch's first-order-recurrence
+// operator).  compose(later, earlier) = later o earlier; associative, not commutative.
+// ------------------------------------------------------------------------------------------------
+template <int S>
+struct Aff {
+  float A[S * S];
+  float b[S];
+};
+
+template <int S>
+DEV Aff<S> aff_id() {
+  Aff<S> m;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) m.A[i * S + j] = (i == j) ? 1.0f : 0.0f;
+    m.b[i] = 0.0f;
+  }
+  return m;
+}
+
+template <int S>
+DEV Aff<S> compose(const Aff<S>& lat, const Aff<S>& ear) {
+  Aff<S> r;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < S; ++k) acc = fmaf(lat.A[i * S + k], ear.A[k * S + j], acc);
+      r.A[i * S + j] = acc;
+    }
+    float acc = lat.b[i];
+#pragma unroll
+    for (int k = 0; k < S; ++k) acc = fmaf(lat.A[i * S + k], ear.b[k], acc);
+    r.b[i] = acc;
+  }
+  return r;
+}
+
+template <int S>
+DEV void apply(const Aff<S>& m, float (&x)[S]) {
+  float y[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    float acc = m.b[i];
+#pragma unroll
+    for (int k = 0; k < S; ++k) acc = fmaf(m.A[i * S + k], x[k], acc);
+    y[i] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < S; ++i) x[i] = y[i];
+}
+
+template <int S>
+DEV float aff_get(const Aff<S>& m, int k) { return k < S * S ? m.A[k] : m.b[k - S * S]; }
+template <int S>
+DEV void aff_set(Aff<S>& m, int k, float v) {
+  if (k < S * S) m.A[k] = v; else m.b[k - S * S] = v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// look-back words: (tag << 32) | float bits, relaxed agent-scope atomics.
+// Layout: word (p, chain, slot, q) at ((p * n_chains + chain) * n_slots + slot) * TW + q, where p is
+// the tile's position in scan order and q its channel within the tile.
+// ------------------------------------------------------------------------------------------------
+DEV uint64_t ld_word(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void st_word(uint64_t* p, uint32_t tag, float v) {
+  const uint64_t w = (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV bool word_ok(uint64_t w, uint32_t tag) { return static_cast<uint32_t>(w >> 32) == tag; }
+DEV float word_val(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+
+struct Common {
+  uint64_t* lb;         // look-back words
+  uint32_t* ticket;     // tile ticket counter of this launch (zeroed before the launch)
+  uint32_t tag;         // nonzero tag of this launch
+  int32_t n_chains;     // channel tiles
+  int64_t n_chunks;     // time chunks
+  int64_t T, D, C, N;   // time steps, channels per row, B*D channels, B*T*D elements
+};
+
+struct Tile {
+  int64_t p, chunk, t_lo, ch0, b, d0;
+  int chain, wave, lane;
+  bool active;
+};
+
+template <int S, int TW, int NSLOT>
+DEV uint64_t* word_at(const Common& c, int64_t p, int chain, int slot, int q) {
+  return c.lb + ((p * c.n_chains + chain) * NSLOT + slot) * static_cast<int64_t>(TW) + q;
+}
+
+// The state entering position p in scan order, for the V channels of one lane.  The words of
+// positions p-1, p-2, ... are read in windows of W; an inclusive word (the state at the end of
+// that chunk) ends the walk, an aggregate word (the chunk's affine map) extends it.  Position 0
+// publishes its inclusive word without waiting, so the walk always ends.
+template <int S, int V, int TW, int NSLOT, int W>
+DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
+  constexpr int NA = S * S + S;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int q = tl.lane * V + v;
+    Aff<S> acc = aff_id<S>();
+    int64_t m = tl.p - 1;
+    bool done = false;
+    while (!done) {
+      uint64_t wi[W][S], wa[W][NA];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const int64_t mm = m - j;
+        if (mm >= 0) {
+#pragma unroll
+          for (int k = 0; k < S; ++k) wi[j][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, k, q));
+#pragma unroll
+          for (int k = 0; k < NA; ++k) wa[j][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, S + k, q));
+        } else {
+#pragma unroll
+          for (int k = 0; k < S; ++k) wi[j][k] = 0;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) wa[j][k] = 0;
+        }
+      }
+      bool stalled = false;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        if (done || stalled) continue;
+        bool inc_ok = true, agg_ok = true;
+#pragma unroll
+        for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[j][k], c.tag);
+#pragma unroll
+        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[j][k], c.tag);
+        if (inc_ok) {
+          float x[S];
+#pragma unroll
+          for (int k = 0; k < S; ++k) x[k] = word_val(wi[j][k]);
+          apply(acc, x);
+#pragma unroll
+          for (int k = 0; k < S; ++k) carry[v][k] = x[k];
+          done = true;
+        } else if (agg_ok) {
+          Aff<S> e;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[j][k]));
+          acc = compose(acc, e);
+          --m;
+        } else {
+          stalled = true;
+        }
+      }
+      if (!done && stalled) __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+DEV float wave_nanmax(float m) {
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) m = nanmax(m, __shfl_xor(m, off, WAVE));
+  return m;
+}
+
+// ------------------------------------------------------------------------------------------------
+// the generic tile kernel
+// ------------------------------------------------------------------------------------------------
+template <class Op>
+__global__ __launch_bounds__(Op::NW * WAVE) void k_tile(const typename Op::Args a) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TW = WAVE * V, NA = S * S + S;
+  constexpr int NSLOT = Op::NSLOT;
+  constexpr bool REV = Op::REVERSE;
+  __shared__ uint32_t sh_ticket;
+  __shared__ float sh_agg[NA][NW][TW];
+  __shared__ float sh_carry[S][TW];
+  __shared__ float sh_red[NW];
+
+  if (Op::skip(a)) return;  // uniform: decided from values written by earlier launches
+  const Common& c = a.c;
+  if (threadIdx.x == 0)
+    sh_ticket = __hip_atomic_fetch_add(c.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  Tile tl;
+  tl.lane = threadIdx.x % WAVE;
+  tl.wave = threadIdx.x / WAVE;
+  tl.p = sh_ticket / static_cast<uint32_t>(c.n_chains);
+  tl.chain = static_cast<int>(sh_ticket % static_cast<uint32_t>(c.n_chains));
+  tl.chunk = REV ? c.n_chunks - 1 - tl.p : tl.p;
+  tl.t_lo = tl.chunk * static_cast<int64_t>(NW * L) + tl.wave * L;
+  tl.ch0 = static_cast<int64_t>(tl.chain) * TW + tl.lane * V;
+  tl.active = tl.ch0 < c.C;
+  tl.b = tl.active ? tl.ch0 / c.D : 0;
+  tl.d0 = tl.active ? tl.ch0 - tl.b * c.D : 0;
+
+  typename Op::Lane ln;
+  float rmax = Op::produce(a, tl, ln);
+
+  // per-lane aggregate over its L steps, in scan order
+  const int q0 = tl.lane * V;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    Aff<S> g = aff_id<S>();
+#pragma unroll
+    for (int s = 0; s < L; ++s) g = compose(ln.e[v][REV ? L - 1 - s : s], g);
+#pragma unroll
+    for (int k = 0; k < NA; ++k) sh_agg[k][tl.wave][q0 + v] = aff_get(g, k);
+  }
+  if constexpr (Op::RESID) {
+    rmax = wave_nanmax(rmax);
+    if (tl.lane == 0) sh_red[tl.wave] = rmax;
+  }
+  __syncthreads();
+  if constexpr (Op::RESID) {
+    if (threadIdx.x == 0) {
+      float m = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) m = nanmax(m, sh_red[w]);
+      atomicMax(a.res_slot, __float_as_uint(m));
+    }
+  }
+
+  if (tl.wave == 0) {
+    float carry[V][S];
+    Aff<S> tagg[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      tagg[v] = aff_id<S>();
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const int w = REV ? NW - 1 - s : s;
+        Aff<S> e;
+#pragma unroll
+        for (int k = 0; k < NA; ++k) aff_set(e, k, sh_agg[k][w][q0 + v]);
+        tagg[v] = compose(e, tagg[v]);
+      }
+    }
+    if (tl.p == 0) {
+      Op::init_state(a, tl, carry);
+    } else {
+      if (tl.active) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < NA; ++k)
+            st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, S + k, q0 + v), c.tag, aff_get(tagg[v], k));
+        lookback<S, V, TW, NSLOT, Op::LB_WINDOW>(c, tl, carry);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S; ++k) carry[v][k] = 0.0f;
+      }
+    }
+    if (tl.active && tl.p + 1 < c.n_chunks) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float x[S];
+#pragma unroll
+        for (int k = 0; k < S; ++k) x[k] = carry[v][k];
+        apply(tagg[v], x);
+#pragma unroll
+        for (int k = 0; k < S; ++k) st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, k, q0 + v), c.tag, x[k]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k) sh_carry[k][q0 + v] = carry[v][k];
+  }
+  __syncthreads();
+
+  // state entering this wave's steps: the tile carry advanced through the waves before it
+  float x[V][S];
+  const int my_pos = REV ? NW - 1 - tl.wave : tl.wave;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float xv[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) xv[k] = sh_carry[k][q0 + v];
+    for (int s = 0; s < my_pos; ++s) {
+      const int w = REV ? NW - 1 - s : s;
+      Aff<S> e;
+#pragma unroll
+      for (int k = 0; k < NA; ++k) aff_set(e, k, sh_agg[k][w][q0 + v]);
+      apply(e, xv);
+    }
+#pragma unroll
+    for (int k = 0; k < S; ++k) x[v][k] = xv[k];
+  }
+  Op::finish(a, tl, ln, x);
+}
+
+// ------------------------------------------------------------------------------------------------
+// cells: value, Jacobian, and (for the VJP) the partials needed by the gate gradients
+// ------------------------------------------------------------------------------------------------
+template <int CELL> struct CellInfo;
+template <> struct CellInfo<CELL_LINEAR> { static constexpr int S = 1, G = 2; };
+template <> struct CellInfo<CELL_GRU> { static constexpr int S = 1, G = 3; };
+template <> struct CellInfo<CELL_LSTM> { static constexpr int S = 2, G = 4; };
+
+// GRU: z = sig(U_z + a_z h + b_z), r = sig(U_r + a_r h + b_r), c = tanh(U_c + a_c r h + b_c),
+//      h' = (1 - z) h + z c,  J = (1 - z) + (c - h) z (1 - z) a_z + z (1 - c^2) a_c (r + h r (1 - r) a_r)
+DEV void gru_eval(float uz, float ur, float uc, float az, float ar, float ac, float bz, float br,
+                  float bc, float h, float& f, float& J) {
+  const float z = sigmoid(fmaf(az, h, uz + bz));
+  const float r = sigmoid(fmaf(ar, h, ur + br));
+  const float c = tanh_(fmaf(ac, r * h, uc + bc));
+  const float cmh = c - h;
+  f = fmaf(z, cmh, h);
+  const float zz = z * (1.0f - z);
+  const float dc = z * fmaf(-c, c, 1.0f);                // z (1 - c^2)
+  const float rr = r * (1.0f - r);
+  J = fmaf(dc * ac, fmaf(h * rr, ar, r), fmaf(cmh * zz, az, 1.0f - z));
+}
+
+// LSTM: i, f, o = sig(U + w h + b), g = tanh(U_g + w_g h + b_g), c' = f c + i g, h' = o tanh(c')
+struct LstmPart {
+  float c2, h2;           // new state
+  float J00, J01, J10, J11;
+  float dc_i, dc_f, dc_g; // d c' / d u_{i,f,g}
+  float dh_o, kh;         // d h' / d u_o, d h' / d c'
+};
+DEV LstmPart lstm_eval(float ui, float uf, float uo, float ug, float wi, float wf, float wo,
+                       float wg, float bi, float bf, float bo, float bg, float c, float h) {
+  LstmPart p;
+  const float ig = sigmoid(fmaf(wi, h, ui + bi));
+  const float fg = sigmoid(fmaf(wf, h, uf + bf));
+  const float og = sigmoid(fmaf(wo, h, uo + bo));
+  const float gg = tanh_(fmaf(wg, h, ug + bg));
+  p.c2 = fmaf(fg, c, ig * gg);
+  const float tc = tanh_(p.c2);
+  p.h2 = og * tc;
+  p.dc_i = gg * ig * (1.0f - ig);
+  p.dc_f = c * fg * (1.0f - fg);
+  p.dc_g = ig * fmaf(-gg, gg, 1.0f);
+  p.kh = og * fmaf(-tc, tc, 1.0f);
+  p.dh_o = tc * og * (1.0f - og);
+  const float dc_dh = fmaf(p.dc_i, wi, fmaf(p.dc_f, wf, p.dc_g * wg));
+  p.J00 = fg;
+  p.J01 = dc_dh;
+  p.J10 = p.kh * fg;
+  p.J11 = fmaf(p.dh_o, wo, p.kh * dc_dh);
+  return p;
+}
+
+// per-lane channel parameters (w, bias) for V channels
+template <int G, int V>
+struct Params {
+  float w[G][V], bias[G][V];
+};
+template <int G, int V>
+DEV void load_params(const float* w, const float* bias, int64_t D, int64_t d0, Params<G, V>& pm) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    ldv<V, DT_F32>(w, g * D + d0, pm.w[g]);
+    ldv<V, DT_F32>(bias, g * D + d0, pm.bias[g]);
+  }
+}
+
+template <int S, int V>
+DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&x)[V][S]) {
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    float t[V];
+    if (s0 && tl.active) {
+      ldv<V, DT_F32>(s0, (k * B + tl.b) * D + tl.d0, t);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) t[v] = 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v][k] = t[v];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Op 1: linear recurrence (pararnn_linear_scan)
+// ------------------------------------------------------------------------------------------------
+template <int S_, int DT, bool REV, int V_, int L_, int NW_>
+struct LinearOp {
+  static constexpr int S = S_, V = V_, L = L_, NW = NW_;
+  static constexpr bool REVERSE = REV, RESID = false;
+  static constexpr int NSLOT = S + S * S + S;
+  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  struct Args {
+    Common c;
+    const void* a;
+    const void* b;
+    const float* s0;
+    float* out;
+    int64_t B;
+    uint32_t* res_slot;  // unused
+  };
+  struct Lane {
+    Aff<S> e[V][L];
+  };
+  static DEV bool skip(const Args&) { return false; }
+  static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
+    load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
+  }
+  static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool ok = tl.active && (tl.t_lo + i < a.c.T);
+      const int64_t idx = base + i * a.c.D;
+      if constexpr (S == 1) {
+        float av[V], bv[V];
+        if (ok) {
+          ldv<V, DT>(a.a, idx, av);
+          ldv<V, DT>(a.b, idx, bv);
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          ln.e[v][i].A[0] = ok ? av[v] : 1.0f;
+          ln.e[v][i].b[0] = ok ? bv[v] : 0.0f;
+        }
+      } else {
+        float av[4][V], bv[2][V];
+        if (ok) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ldv<V, DT>(a.a, k * a.c.N + idx, av[k]);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) ldv<V, DT>(a.b, k * a.c.N + idx, bv[k]);
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          if (ok) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ln.e[v][i].A[k] = av[k][v];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) ln.e[v][i].b[k] = bv[k][v];
+          } else {
+            ln.e[v][i] = aff_id<S>();
+          }
+        }
+      }
+    }
+    return 0.0f;
+  }
+  static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
+    if (!tl.active) return;
+    const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
+#pragma unroll
+    for (int s = 0; s < L; ++s) {
+      const int i = REV ? L - 1 - s : s;
+      if (tl.t_lo + i >= a.c.T) continue;
+#pragma unroll
+      for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = x[v][k];
+        stv<V>(a.out + k * a.c.N + base + i * a.c.D, o);
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// Op 2: one fused Newton iteration (pararnn_newton_solve)
+//   element of step t:  A_t = J_t,  b_t = f_t - J_t h^k_{t-1}   (f_t, J_t at (h^k_{t-1}, x_t))
+//   so that the scan gives h^{k+1}_t = h^k_t + delta_t with delta_t = J_t delta_{t-1} - r_t,
+//   r_t = h^k_t - f_t (the same iterate, written without forming delta).  The max |r_t| is
+//   reduced for the tolerance test.  LINEAR: the element is (a_t, b_t) itself.
+// ------------------------------------------------------------------------------------------------
+template <int CELL, int DT, int V_, int L_, int NW_>
+struct NewtonOp {
+  static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
+  static constexpr int V = V_, L = L_, NW = NW_;
+  static constexpr bool REVERSE = false, RESID = true;
+  static constexpr int HALO = S + S * S + S;          // slot of the halo words
+  static constexpr int NSLOT = HALO + S;
+  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  struct Args {
+    Common c;
+    const void* pre[4];
+    const float* w;
+    const float* bias;
+    const float* s0;
+    const float* h_in;        // H^k [S][B][T][D], or NULL for H^k = 0
+    float* h_out;             // H^{k+1}; may equal h_in
+    uint32_t* res_slot;       // max |r| of this iteration (float bits, atomicMax)
+    const uint32_t* res_hist; // max |r| of earlier iterations
+    int32_t k;
+    float tol;
+    int64_t B;
+  };
+  struct Lane {
+    Aff<S> e[V][L];
+  };
+  static DEV bool skip(const Args& a) {
+    if (!(a.tol > 0.0f)) return false;
+    for (int j = 0; j < a.k; ++j) {
+      const float r = __uint_as_float(a.res_hist[j]);
+      if (!(r >= a.tol) || r == INFINITY) return true;  // converged, or NaN / Inf: stop
+    }
+    return false;
+  }
+  static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
+    load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
+  }
+  static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
+    float rmax = 0.0f;
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
+    const Common& c = a.c;
+    constexpr int TW = WAVE * V;
+    const int q0 = tl.lane * V;
+    if (!tl.active) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int i = 0; i < L; ++i) ln.e[v][i] = aff_id<S>();
+      return 0.0f;
+    }
+    const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
+    // current iterate at steps t_lo-1 .. t_lo+L-1 (index 0 is the step before the lane's first)
+    float h[S][L + 1][V];
+    const bool have_h = a.h_in != nullptr;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool ok = tl.t_lo + i < T;
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        if (have_h && ok) {
+          ldv<V, DT_F32>(a.h_in, k * N + base + i * D, h[k][i + 1]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) h[k][i + 1][v] = 0.0f;
+        }
+      }
+    }
+    float u[G][L][V];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool ok = tl.t_lo + i < T;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (ok) {
+          ldv<V, DT>(a.pre[g], base + i * D, u[g][i]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) u[g][i][v] = 0.0f;
+        }
+      }
+    }
+    // the state before the lane's first step
+    if (tl.t_lo == 0) {
+      float x[V][S];
+      load_s0<S, V>(a.s0, a.B, D, tl, x);
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) h[k][0][v] = x[v][k];
+    } else if (!have_h) {
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) h[k][0][v] = 0.0f;
+    } else if (tl.wave != 0) {
+      // h^k_{t_lo-1} lies in this tile (written only after the tile's look-back); a lane whose
+      // steps all lie past T reads nothing
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        if (tl.t_lo <= T) {
+          ldv<V, DT_F32>(a.h_in, k * N + base - D, h[k][0]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) h[k][0][v] = 0.0f;
+        }
+      }
+    }
+    if (have_h) {
+      // publish this tile's last state (the h^k the next tile's first step needs), then take the
+      // previous tile's: the trajectory is updated in place, so it cannot be re-read from memory
+      if (tl.wave == NW - 1 && tl.t_lo + L - 1 < T && tl.p + 1 < c.n_chunks) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S; ++k)
+            st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, HALO + k, q0 + v), c.tag, h[k][L][v]);
+      }
+      if (tl.wave == 0 && tl.t_lo != 0) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S; ++k) {
+            const uint64_t* wp = word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, HALO + k, q0 + v);
+            uint64_t wv = ld_word(wp);
+            while (!word_ok(wv, c.tag)) {
+              __builtin_amdgcn_s_sleep(1);
+              wv = ld_word(wp);
+            }
+            h[k][0][v] = word_val(wv);
+          }
+      }
+    }
+    Params<G, V> pm;
+    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(a.w, a.bias, D, tl.d0, pm);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool ok = tl.t_lo + i < T;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (!ok) {
+          ln.e[v][i] = aff_id<S>();
+          continue;
+        }
+        if constexpr (CELL == CELL_LINEAR) {
+          const float hp = h[0][i][v];
+          const float f = fmaf(u[0][i][v], hp, u[1][i][v]);
+          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - f));
+          ln.e[v][i].A[0] = u[0][i][v];
+          ln.e[v][i].b[0] = u[1][i][v];
+        } else if constexpr (CELL == CELL_GRU) {
+          const float hp = h[0][i][v];
+          float f, J;
+          gru_eval(u[0][i][v], u[1][i][v], u[2][i][v], pm.w[0][v], pm.w[1][v], pm.w[2][v],
+                   pm.bias[0][v], pm.bias[1][v], pm.bias[2][v], hp, f, J);
+          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - f));
+          ln.e[v][i].A[0] = J;
+          ln.e[v][i].b[0] = fmaf(-J, hp, f);
+        } else {
+          const float cp = h[0][i][v], hp = h[1][i][v];
+          const LstmPart q = lstm_eval(u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], pm.w[0][v],
+                                       pm.w[1][v], pm.w[2][v], pm.w[3][v], pm.bias[0][v],
+                                       pm.bias[1][v], pm.bias[2][v], pm.bias[3][v], cp, hp);
+          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - q.c2));
+          rmax = nanmax(rmax, fabsf(h[1][i + 1][v] - q.h2));
+          Aff<2>& e = ln.e[v][i];
+          e.A[0] = q.J00; e.A[1] = q.J01; e.A[2] = q.J10; e.A[3] = q.J11;
+          e.b[0] = q.c2 - fmaf(q.J00, cp, q.J01 * hp);
+          e.b[1] = q.h2 - fmaf(q.J10, cp, q.J11 * hp);
+        }
+      }
+    }
+    return rmax;
+  }
+  static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
+    if (!tl.active) return;
+    const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (tl.t_lo + i >= a.c.T) continue;
+#pragma unroll
+      for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = x[v][k];
+        stv<V>(a.h_out + k * a.c.N + base + i * a.c.D, o);
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// Op 3: VJP by one reverse scan (pararnn_scan_vjp)
+//   element of step t:  A_t = J_{t+1}^T (0 at t = T-1),  b_t = e_h g_t   ->  lambda_t
+//   then dU_{gate,t} = lambda_t . d f/d u_gate at (s_{t-1}, x_t), and per-tile parameter partials.
+// ------------------------------------------------------------------------------------------------
+template <int CELL> struct VjpStash;
+template <> struct VjpStash<CELL_LINEAR> { float hp; };
+template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
+template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
+
+template <int CELL, int DT, int V_, int L_, int NW_>
+struct VjpOp {
+  static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
+  static constexpr int V = V_, L = L_, NW = NW_;
+  static constexpr bool REVERSE = true, RESID = false;
+  static constexpr int NSLOT = S + S * S + S;
+  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
+  struct Args {
+    Common c;
+    const void* pre[4];
+    const float* w;
+    const float* bias;
+    const float* s0;
+    const float* s;       // trajectory [S][B][T][D]
+    const float* g;       // [B][T][D]
+    float* d_pre;         // [G][B][T][D]
+    float* lambda_out;    // [S][B][T][D] or NULL
+    float* d_s0;          // [S][B][D] or NULL
+    float* partial;       // [n_chunks][NPAR][C]
+    int64_t B;
+    uint32_t* res_slot;   // unused
+  };
+  struct Lane {
+    Aff<S> e[V][L];
+    VjpStash<CELL> st[V][L];
+    float J0[V][S * S];   // Jacobian at step 0 (only used by the lane that owns t = 0)
+  };
+  static DEV bool skip(const Args&) { return false; }
+  static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k) x[v][k] = 0.0f;   // nothing flows in from beyond the last step
+  }
+  static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S * S; ++k) ln.J0[v][k] = 0.0f;
+    if (!tl.active) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int i = 0; i < L; ++i) ln.e[v][i] = aff_id<S>();
+      return 0.0f;
+    }
+    const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
+    Params<G, V> pm;
+    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(a.w, a.bias, D, tl.d0, pm);
+    // evaluations e = L .. 0 at time t_lo + e (e = L is the first step of the next lane / chunk)
+    float Jn[V][S * S];   // Jacobian of evaluation e+1, transposed into the element of step e
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S * S; ++k) Jn[v][k] = 0.0f;
+#pragma unroll
+    for (int e = L; e >= 0; --e) {
+      const int64_t t = tl.t_lo + e;
+      const bool ok = t < T;
+      float u[G][V], sp[S][V], gv[V];
+      if (ok) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], base + e * D, u[g]);
+        if (t == 0) {
+          float x[V][S];
+          load_s0<S, V>(a.s0, a.B, D, tl, x);
+#pragma unroll
+          for (int k = 0; k < S; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) sp[k][v] = x[v][k];
+        } else {
+#pragma unroll
+          for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + base + (e - 1) * D, sp[k]);
+        }
+        if (e < L) ldv<V, DT_F32>(a.g, base + e * D, gv);
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float J[S * S];
+#pragma unroll
+        for (int k = 0; k < S * S; ++k) J[k] = 0.0f;
+        VjpStash<CELL> st{};
+        if (ok) {
+          if constexpr (CELL == CELL_LINEAR) {
+            J[0] = u[0][v];
+            st.hp = sp[0][v];
+          } else if constexpr (CELL == CELL_GRU) {
+            const float hp = sp[0][v];
+            const float az = pm.w[0][v], ar = pm.w[1][v], ac = pm.w[2][v];
+            const float z = sigmoid(fmaf(az, hp, u[0][v] + pm.bias[0][v]));
+            const float r = sigmoid(fmaf(ar, hp, u[1][v] + pm.bias[1][v]));
+            const float cc = tanh_(fmaf(ac, r * hp, u[2][v] + pm.bias[2][v]));
+            const float cmh = cc - hp;
+            const float zz = z * (1.0f - z);
+            const float dc = z * fmaf(-cc, cc, 1.0f);
+            const float rr = r * (1.0f - r);
+            J[0] = fmaf(dc * ac, fmaf(hp * rr, ar, r), fmaf(cmh * zz, az, 1.0f - z));
+            st.pz = cmh * zz;
+            st.pc = dc;
+            st.hp = hp;
+            st.r = r;
+          } else {
+            const LstmPart q = lstm_eval(u[0][v], u[1][v], u[2][v], u[3][v], pm.w[0][v], pm.w[1][v],
+                                         pm.w[2][v], pm.w[3][v], pm.bias[0][v], pm.bias[1][v],
+                                         pm.bias[2][v], pm.bias[3][v], sp[0][v], sp[1][v]);
+            J[0] = q.J00; J[1] = q.J01; J[2] = q.J10; J[3] = q.J11;
+            st.dci = q.dc_i; st.dcf = q.dc_f; st.dcg = q.dc_g; st.dho = q.dh_o; st.kh = q.kh;
+            st.hp = sp[1][v];
+          }
+        }
+        if (e < L) {
+          Aff<S>& el = ln.e[v][e];
+          if (ok) {
+            // A = J_{t+1}^T
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+#pragma unroll
+              for (int j = 0; j < S; ++j) el.A[i * S + j] = Jn[v][j * S + i];
+#pragma unroll
+            for (int k = 0; k < S; ++k) el.b[k] = 0.0f;
+            el.b[S - 1] = gv[v];
+            ln.st[v][e] = st;
+            if (t == 0) {
+#pragma unroll
+              for (int k = 0; k < S * S; ++k) ln.J0[v][k] = J[k];
+            }
+          } else {
+            el = aff_id<S>();
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < S * S; ++k) Jn[v][k] = ok ? J[k] : 0.0f;
+      }
+    }
+    return 0.0f;
+  }
+  static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
+    constexpr int TW = WAVE * V;
+    constexpr int NP = NPAR > 0 ? NPAR : 1;
+    __shared__ float sh_par[NP][NW][TW];
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
+    float par[V][NP];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int j = 0; j < NP; ++j) par[v][j] = 0.0f;
+    if (tl.active) {
+      const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
+#pragma unroll
+      for (int s = 0; s < L; ++s) {
+        const int i = L - 1 - s;
+        const int64_t t = tl.t_lo + i;
+        if (t >= T) continue;
+        float du[G][V], lam[S][V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          apply(ln.e[v][i], x[v]);
+          const VjpStash<CELL>& st = ln.st[v][i];
+#pragma unroll
+          for (int k = 0; k < S; ++k) lam[k][v] = x[v][k];
+          if constexpr (CELL == CELL_LINEAR) {
+            du[0][v] = x[v][0] * st.hp;
+            du[1][v] = x[v][0];
+          } else if constexpr (CELL == CELL_GRU) {
+            const float l = x[v][0];
+            const float ac = a.w[2 * D + tl.d0 + v];
+            du[0][v] = l * st.pz;
+            du[2][v] = l * st.pc;
+            du[1][v] = du[2][v] * ac * st.hp * st.r * (1.0f - st.r);
+            par[v][0] = fmaf(du[0][v], st.hp, par[v][0]);
+            par[v][1] = fmaf(du[1][v], st.hp, par[v][1]);
+            par[v][2] = fmaf(du[2][v], st.r * st.hp, par[v][2]);
+#pragma unroll
+            for (int g = 0; g < 3; ++g) par[v][3 + g] += du[g][v];
+          } else {
+            const float lc = x[v][0], lh = x[v][1];
+            const float m = fmaf(st.kh, lh, lc);   // lambda_c + kh lambda_h
+            du[0][v] = m * st.dci;
+            du[1][v] = m * st.dcf;
+            du[2][v] = lh * st.dho;
+            du[3][v] = m * st.dcg;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              par[v][g] = fmaf(du[g][v], st.hp, par[v][g]);
+              par[v][4 + g] += du[g][v];
+            }
+          }
+          if (t == 0 && a.d_s0) {
+#pragma unroll
+            for (int i2 = 0; i2 < S; ++i2) {
+              float acc = 0.0f;
+#pragma unroll
+              for (int j = 0; j < S; ++j) acc = fmaf(ln.J0[v][j * S + i2], x[v][j], acc);
+              a.d_s0[(i2 * a.B + tl.b) * D + tl.d0 + v] = acc;
+            }
+          }
+        }
+        const int64_t idx = base + i * D;
+#pragma unroll
+        for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
+        if (a.lambda_out) {
+#pragma unroll
+          for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);
+        }
+      }
+    }
+    if constexpr (NPAR > 0) {
+      const int q0 = tl.lane * V;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int j = 0; j < NPAR; ++j) sh_par[j][tl.wave][q0 + v] = par[v][j];
+      __syncthreads();
+      // fixed-order sum over the waves of the tile
+      for (int idx = threadIdx.x; idx < NPAR * TW; idx += NW * WAVE) {
+        const int j = idx / TW, q = idx % TW;
+        const int64_t ch = static_cast<int64_t>(tl.chain) * TW + q;
+        if (ch >= a.c.C) continue;
+        float sum = 0.0f;
+        for (int w = 0; w < NW; ++w) sum += sh_par[j][w][q];
+        a.partial[(tl.chunk * NPAR + j) * a.c.C + ch] = sum;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// auxiliary kernels
+// ------------------------------------------------------------------------------------------------
+// zero-fill (used instead of hipMemsetAsync so that the calls stay capturable)
+__global__ void k_zero(uint4* p, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// fixed-order reduction of the VJP parameter partials: out[j][d] = sum_b sum_chunk partial[chunk][j][b*D+d]
+__global__ void k_param_reduce(const float* partial, int64_t n_chunks, int npar, int64_t B, int64_t D,
+                               float* d_w, float* d_bias, int G) {
+  const int64_t C = B * D;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= npar * D) return;
+  const int j = static_cast<int>(i / D);
+  const int64_t d = i - j * D;
+  float sum = 0.0f;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t ch = 0; ch < n_chunks; ++ch) sum += partial[(ch * npar + j) * C + b * D + d];
+  if (j < G) {
+    if (d_w) d_w[j * D + d] = sum;
+  } else {
+    if (d_bias) d_bias[(j - G) * D + d] = sum;
+  }
+}
+
+// max |h_t - f(h_{t-1}, x_t)| of a trajectory (the optional final-residual pass); one thread per
+// V channels x L steps, read-only
+template <int CELL, int DT, int V, int L>
+__global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1, const void* p2,
+                                                  const void* p3, const float* w, const float* bias,
+                                                  const float* s0, const float* h, int64_t B, int64_t T,
+                                                  int64_t D, uint32_t* out) {
+  constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
+  const void* pre[4] = {p0, p1, p2, p3};
+  const int64_t C = B * D, N = B * T * D;
+  const int64_t n_col = (C + V - 1) / V;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t col = gid % n_col, chunk = gid / n_col;
+  float m = 0.0f;
+  if (chunk * L < T && col * V < C) {
+    const int64_t ch0 = col * V, b = ch0 / D, d0 = ch0 - b * D;
+    Params<G, V> pm;
+    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(w, bias, D, d0, pm);
+    for (int i = 0; i < L; ++i) {
+      const int64_t t = chunk * L + i;
+      if (t >= T) break;
+      const int64_t idx = (b * T + t) * D + d0;
+      float prev[S][V], cur[S][V], u[G][V];
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        if (t == 0) {
+          if (s0) ldv<V, DT_F32>(s0, (k * B + b) * D + d0, prev[k]);
+          else
+#pragma unroll
+            for (int v = 0; v < V; ++v) prev[k][v] = 0.0f;
+        } else {
+          ldv<V, DT_F32>(h, k * N + idx - D, prev[k]);
+        }
+        ldv<V, DT_F32>(h, k * N + idx, cur[k]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) ldv<V, DT>(pre[g], idx, u[g]);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if constexpr (CELL == CELL_LINEAR) {
+          m = nanmax(m, fabsf(cur[0][v] - fmaf(u[0][v], prev[0][v], u[1][v])));
+        } else if constexpr (CELL == CELL_GRU) {
+          float f, J;
+          gru_eval(u[0][v], u[1][v], u[2][v], pm.w[0][v], pm.w[1][v], pm.w[2][v], pm.bias[0][v],
+                   pm.bias[1][v], pm.bias[2][v], prev[0][v], f, J);
+          m = nanmax(m, fabsf(cur[0][v] - f));
+        } else {
+          const LstmPart q = lstm_eval(u[0][v], u[1][v], u[2][v], u[3][v], pm.w[0][v], pm.w[1][v],
+                                       pm.w[2][v], pm.w[3][v], pm.bias[0][v], pm.bias[1][v],
+                                       pm.bias[2][v], pm.bias[3][v], prev[0][v], prev[1][v]);
+          m = nanmax(m, fabsf(cur[0][v] - q.c2));
+          m = nanmax(m, fabsf(cur[1][v] - q.h2));
+        }
+      }
+    }
+  }
+  m = wave_nanmax(m);
+  if ((threadIdx.x % WAVE) == 0) atomicMax(out, __float_as_uint(m));
+}
+
+}  // namespace pr
+
+// ================================================================================================
+// host side
+// ================================================================================================
+namespace {
+
+using namespace pr;
+
+std::atomic<uint32_t> g_tag{0};
+uint32_t next_tag() {
+  uint32_t t;
+  do {
+    t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (t == 0);
+  return t;
+}
+
+int state_size(int cell) { return cell == CELL_LSTM ? 2 : 1; }
+int gate_count(int cell) { return cell == CELL_LSTM ? 4 : (cell == CELL_GRU ? 3 : 2); }
+
+// workspace: [header 4 KiB: tickets, residual slots][look-back words][VJP partials]
+constexpr size_t kHeader = 4096;
+constexpr size_t kResOffset = 2048;  // residual slots (uint32 float bits) inside the header
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Geo {
+  int V, L, NW, S, nslot;
+  int64_t TW, CT, n_chains, n_chunks;
+  size_t lb_bytes() const {
+    return static_cast<size_t>(n_chunks) * n_chains * nslot * TW * sizeof(uint64_t);
+  }
+};
+
+Geo make_geo(int S, int nslot, int V, int L, int NW, int64_t B, int64_t T, int64_t D) {
+  Geo g;
+  g.V = V; g.L = L; g.NW = NW; g.S = S; g.nslot = nslot;
+  g.TW = WAVE * V;
+  g.CT = static_cast<int64_t>(NW) * L;
+  const int64_t C = B * D;
+  g.n_chains = (C + g.TW - 1) / g.TW;
+  g.n_chunks = (T + g.CT - 1) / g.CT;
+  return g;
+}
+
+// tile configurations (V channels per lane, L steps per lane, NW waves per workgroup); the same
+// values instantiate the kernels and size the workspaces
+template <int CELL> struct NewtonCfg { static constexpr int V = CELL == CELL_LSTM ? 1 : 2, L = 8, NW = 16; };
+template <int S> struct ScanCfg { static constexpr int V = 1, L = S == 1 ? 16 : 8, NW = 16; };
+template <int CELL> struct VjpCfg { static constexpr int V = 1, L = CELL == CELL_LSTM ? 4 : 8, NW = 16; };
+
+Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int ticket_slot) {
+  Common c;
+  char* base = static_cast<char*>(ws);
+  c.lb = reinterpret_cast<uint64_t*>(base + kHeader);
+  c.ticket = reinterpret_cast<uint32_t*>(base) + ticket_slot;
+  c.tag = 0;
+  c.n_chains = static_cast<int32_t>(g.n_chains);
+  c.n_chunks = g.n_chunks;
+  c.T = T; c.D = D; c.C = B * D; c.N = B * T * D;
+  return c;
+}
+
+pararnn_status launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return PARARNN_OK;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n16);
+  return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
+template <class Op>
+pararnn_status launch_tile(const typename Op::Args& a, const Geo& g, hipStream_t st) {
+  const int64_t tiles = g.n_chains * g.n_chunks;
+  if (tiles <= 0) return PARARNN_OK;
+  hipLaunchKernelGGL(k_tile<Op>, dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a);
+  return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
+bool grid_ok(const Geo& g) {
+  const int64_t tiles = g.n_chains * g.n_chunks;
+  return tiles < (static_cast<int64_t>(1) << 31);
+}
+
+// ---------------- validation ----------------
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pararnn_status check_problem(const pararnn_problem* pb) {
+  if (!pb) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cell < 0 || pb->cell > 2) return PARARNN_ERR_INVALID_ARG;
+  if (pb->pre_dtype != PARARNN_F32 && pb->pre_dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
+  if (pb->B < 0 || pb->T < 0 || pb->D < 0) return PARARNN_ERR_INVALID_ARG;
+  if (pb->B > (int64_t(1) << 40) || pb->D > (int64_t(1) << 40)) return PARARNN_ERR_INVALID_ARG;
+  if (pb->B > 0 && pb->D > 0 && pb->T > INT64_MAX / (pb->B * pb->D) / 4) return PARARNN_ERR_INVALID_ARG;
+  const int64_t N = pb->B * pb->T * pb->D;
+  if (N == 0) return PARARNN_OK;
+  if (pb->D % 2 != 0) return PARARNN_ERR_UNSUPPORTED;
+  const int G = gate_count(pb->cell);
+  for (int g = 0; g < G; ++g)
+    if (!pb->pre[g] || !aligned(pb->pre[g], 8)) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cell != CELL_LINEAR && (!pb->w || !pb->bias || !aligned(pb->w, 8) || !aligned(pb->bias, 8)))
+    return PARARNN_ERR_INVALID_ARG;
+  if (pb->s0 && !aligned(pb->s0, 8)) return PARARNN_ERR_INVALID_ARG;
+  return PARARNN_OK;
+}
+
+int64_t problem_N(const pararnn_problem* pb) { return pb->B * pb->T * pb->D; }
+
+// ---------------- Newton ----------------
+template <int CELL, int DT>
+struct NewtonKernel {
+  using C = NewtonCfg<CELL>;
+  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW>;
+  static Geo geo(const pararnn_problem* pb) {
+    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
+  }
+  static size_t ws(const pararnn_problem* pb) { return kHeader + align256(geo(pb).lb_bytes()); }
+  static pararnn_status run(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out, void* ws,
+                            hipStream_t st) {
+    const Geo g = geo(pb);
+    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+    pararnn_status rc = launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
+    if (rc) return rc;
+    uint32_t* res = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kResOffset);
+    for (int k = 0; k < op->max_iters; ++k) {
+      typename Op::Args a;
+      a.c = make_common(ws, g, pb->B, pb->T, pb->D, k);
+      a.c.tag = next_tag();
+      for (int i = 0; i < 4; ++i) a.pre[i] = pb->pre[i];
+      a.w = pb->w;
+      a.bias = pb->bias;
+      a.s0 = pb->s0;
+      a.h_in = (k == 0) ? op->init_guess : s_out;
+      a.h_out = s_out;
+      a.res_slot = res + k;
+      a.res_hist = res;
+      a.k = k;
+      a.tol = op->tol;
+      a.B = pb->B;
+      rc = launch_tile<Op>(a, g, st);
+      if (rc) return rc;
+    }
+    if (op->final_residual) {
+      constexpr int RV = 2, RL = 16;
+      const int64_t C = pb->B * pb->D;
+      const int64_t threads = ((C + RV - 1) / RV) * ((pb->T + RL - 1) / RL);
+      const int64_t blocks = (threads + 255) / 256;
+      hipLaunchKernelGGL((k_residual<CELL, DT, RV, RL>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                         pb->pre[0], pb->pre[1], pb->pre[2], pb->pre[3], pb->w, pb->bias, pb->s0, s_out, pb->B,
+                         pb->T, pb->D, res + PARARNN_MAX_ITERS);
+      if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    return PARARNN_OK;
+  }
+};
+
+struct NewtonEntry {
+  size_t (*ws)(const pararnn_problem*);
+  pararnn_status (*run)(const pararnn_problem*, const pararnn_newton_opts*, float*, void*, hipStream_t);
+};
+
+template <int CELL, int DT>
+NewtonEntry newton_entry() { return {NewtonKernel<CELL, DT>::ws, NewtonKernel<CELL, DT>::run}; }
+
+NewtonEntry pick_newton(int cell, int dt) {
+  if (cell == CELL_GRU) return dt == DT_BF16 ? newton_entry<CELL_GRU, DT_BF16>() : newton_entry<CELL_GRU, DT_F32>();
+  if (cell == CELL_LSTM) return dt == DT_BF16 ? newton_entry<CELL_LSTM, DT_BF16>() : newton_entry<CELL_LSTM, DT_F32>();
+  return dt == DT_BF16 ? newton_entry<CELL_LINEAR, DT_BF16>() : newton_entry<CELL_LINEAR, DT_F32>();
+}
+
+// ---------------- linear scan ----------------
+template <int S, int DT, bool REV>
+struct ScanKernel {
+  using C = ScanCfg<S>;
+  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW>;
+  static Geo geo(int64_t B, int64_t T, int64_t D) { return make_geo(S, Op::NSLOT, C::V, C::L, C::NW, B, T, D); }
+  static size_t ws(int64_t B, int64_t T, int64_t D) { return kHeader + align256(geo(B, T, D).lb_bytes()); }
+  static pararnn_status run(int64_t B, int64_t T, int64_t D, const void* a_, const void* b_, const float* s0,
+                            float* out, void* ws, hipStream_t st) {
+    const Geo g = geo(B, T, D);
+    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+    pararnn_status rc = launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
+    if (rc) return rc;
+    typename Op::Args a;
+    a.c = make_common(ws, g, B, T, D, 0);
+    a.c.tag = next_tag();
+    a.a = a_;
+    a.b = b_;
+    a.s0 = s0;
+    a.out = out;
+    a.B = B;
+    a.res_slot = nullptr;
+    return launch_tile<Op>(a, g, st);
+  }
+};
+
+struct ScanEntry {
+  size_t (*ws)(int64_t, int64_t, int64_t);
+  pararnn_status (*run)(int64_t, int64_t, int64_t, const void*, const void*, const float*, float*, void*, hipStream_t);
+};
+
+template <int S, int DT, bool REV>
+ScanEntry scan_entry() { return {ScanKernel<S, DT, REV>::ws, ScanKernel<S, DT, REV>::run}; }
+
+template <int S, int DT>
+ScanEntry pick_scan_dir(int rev) { return rev ? scan_entry<S, DT, true>() : scan_entry<S, DT, false>(); }
+
+ScanEntry pick_scan(int S, int dt, int rev) {
+  if (S == 1) return dt == DT_BF16 ? pick_scan_dir<1, DT_BF16>(rev) : pick_scan_dir<1, DT_F32>(rev);
+  return dt == DT_BF16 ? pick_scan_dir<2, DT_BF16>(rev) : pick_scan_dir<2, DT_F32>(rev);
+}
+
+// ---------------- VJP ----------------
+template <int CELL, int DT>
+struct VjpKernel {
+  using C = VjpCfg<CELL>;
+  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW>;
+  static Geo geo(const pararnn_problem* pb) {
+    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
+  }
+  static size_t part_bytes(const Geo& g, const pararnn_problem* pb) {
+    return static_cast<size_t>(g.n_chunks) * Op::NPAR * pb->B * pb->D * sizeof(float);
+  }
+  static size_t ws(const pararnn_problem* pb) {
+    const Geo g = geo(pb);
+    return kHeader + align256(g.lb_bytes()) + align256(part_bytes(g, pb));
+  }
+  static pararnn_status run(const pararnn_problem* pb, const float* s, const float* gr, float* d_pre, float* d_w,
+                            float* d_bias, float* d_s0, float* lam, void* ws, hipStream_t st) {
+    const Geo g = geo(pb);
+    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+    const size_t lbb = align256(g.lb_bytes());
+    pararnn_status rc = launch_zero(ws, kHeader + lbb, st);
+    if (rc) return rc;
+    typename Op::Args a;
+    a.c = make_common(ws, g, pb->B, pb->T, pb->D, 0);
+    a.c.tag = next_tag();
+    for (int i = 0; i < 4; ++i) a.pre[i] = pb->pre[i];
+    a.w = pb->w;
+    a.bias = pb->bias;
+    a.s0 = pb->s0;
+    a.s = s;
+    a.g = gr;
+    a.d_pre = d_pre;
+    a.lambda_out = lam;
+    a.d_s0 = d_s0;
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kHeader + lbb);
+    a.B = pb->B;
+    a.res_slot = nullptr;
+    rc = launch_tile<Op>(a, g, st);
+    if (rc) return rc;
+    if constexpr (Op::NPAR > 0) {
+      if (d_w || d_bias) {
+        const int64_t n = Op::NPAR * pb->D;
+        hipLaunchKernelGGL(k_param_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                           a.partial, g.n_chunks, Op::NPAR, pb->B, pb->D, d_w, d_bias, Op::G);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+      }
+    }
+    return PARARNN_OK;
+  }
+};
+
+struct VjpEntry {
+  size_t (*ws)(const pararnn_problem*);
+  pararnn_status (*run)(const pararnn_problem*, const float*, const float*, float*, float*, float*, float*, float*,
+                        void*, hipStream_t);
+};
+
+template <int CELL, int DT>
+VjpEntry vjp_entry() { return {VjpKernel<CELL, DT>::ws, VjpKernel<CELL, DT>::run}; }
+
+VjpEntry pick_vjp(int cell, int dt) {
+  if (cell == CELL_GRU) return dt == DT_BF16 ? vjp_entry<CELL_GRU, DT_BF16>() : vjp_entry<CELL_GRU, DT_F32>();
+  if (cell == CELL_LSTM) return dt == DT_BF16 ? vjp_entry<CELL_LSTM, DT_BF16>() : vjp_entry<CELL_LSTM, DT_F32>();
+  return dt == DT_BF16 ? vjp_entry<CELL_LINEAR, DT_BF16>() : vjp_entry<CELL_LINEAR, DT_F32>();
+}
+
+}  // namespace
+
+// ================================================================================================
+// C ABI
+// ================================================================================================
+extern "C" {
+
+int pararnn_abi_version(void) { return PARARNN_ABI_VERSION; }
+
+const char* pararnn_status_string(int s) {
+  switch (s) {
+    case PARARNN_OK: return "ok";
+    case PARARNN_ERR_INVALID_ARG: return "invalid argument";
+    case PARARNN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PARARNN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PARARNN_ERR_HIP: return "HIP runtime error";
+    case PARARNN_ERR_DIVERGED: return "Newton diverged (non-finite residual)";
+    default: return "unknown status";
+  }
+}
+
+size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_newton_opts*) {
+  if (check_problem(pb) != PARARNN_OK) return 0;
+  if (problem_N(pb) == 0) return kHeader;
+  return pick_newton(pb->cell, pb->pre_dtype).ws(pb);
+}
+
+pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out, void* ws,
+                                    size_t ws_bytes, void* stream, pararnn_report* report) {
+  pararnn_status rc = check_problem(pb);
+  if (rc) return rc;
+  if (!op || op->max_iters < 1 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (report) std::memset(report, 0, sizeof(*report));
+  const int64_t N = problem_N(pb);
+  if (N == 0) {
+    if (report) report->converged = op->tol > 0.0f ? 1 : 0;
+    return PARARNN_OK;
+  }
+  if (!s_out || !aligned(s_out, 8)) return PARARNN_ERR_INVALID_ARG;
+  if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
+  const NewtonEntry ne = pick_newton(pb->cell, pb->pre_dtype);
+  if (!ws || !aligned(ws, 256) || ws_bytes < ne.ws(pb)) return PARARNN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = ne.run(pb, op, s_out, ws, st);
+  if (rc || !report) return rc;
+  uint32_t res[PARARNN_MAX_ITERS + 1];
+  if (hipMemcpyAsync(res, static_cast<char*>(ws) + kResOffset, sizeof(res), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return PARARNN_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return PARARNN_ERR_HIP;
+  int iters = op->max_iters, conv = 0;
+  pararnn_status out = PARARNN_OK;
+  for (int k = 0; k < op->max_iters; ++k) {
+    float r;
+    std::memcpy(&r, &res[k], sizeof r);
+    report->residual[k] = r;
+    if (op->tol > 0.0f) {
+      if (!(r >= 0.0f) || r == INFINITY) { iters = k + 1; out = PARARNN_ERR_DIVERGED; break; }
+      if (r < op->tol) { iters = k + 1; conv = 1; break; }
+    }
+  }
+  report->iters = iters;
+  report->converged = conv;
+  report->n_residual = iters;
+  if (op->final_residual) {
+    float r;
+    std::memcpy(&r, &res[PARARNN_MAX_ITERS], sizeof r);
+    report->residual[iters] = r;
+    report->n_residual = iters + 1;
+  }
+  return out;
+}
+
+size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {
+  if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return 0;
+  if (B * T * D == 0) return kHeader;
+  return pick_scan(S, PARARNN_F32, 0).ws(B, T, D);
+}
+
+pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void* a, const void* b,
+                                   const float* s0, float* s_out, int reverse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return PARARNN_ERR_INVALID_ARG;
+  if (dtype != PARARNN_F32 && dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
+  if (B > 0 && D > 0 && T > INT64_MAX / (B * D) / 4) return PARARNN_ERR_INVALID_ARG;
+  if (B * T * D == 0) return PARARNN_OK;
+  if (!a || !b || !s_out) return PARARNN_ERR_INVALID_ARG;
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(s_out, 4) || (s0 && !aligned(s0, 4))) return PARARNN_ERR_INVALID_ARG;
+  const ScanEntry se = pick_scan(S, dtype, reverse ? 1 : 0);
+  if (!ws || !aligned(ws, 256) || ws_bytes < se.ws(B, T, D)) return PARARNN_ERR_WORKSPACE;
+  return se.run(B, T, D, a, b, s0, s_out, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t pararnn_vjp_workspace_bytes(const pararnn_problem* pb) {
+  if (check_problem(pb) != PARARNN_OK) return 0;
+  if (problem_N(pb) == 0) return kHeader;
+  return pick_vjp(pb->cell, pb->pre_dtype).ws(pb);
+}
+
+pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const float* g, float* d_pre, float* d_w,
+                                float* d_bias, float* d_s0, float* lambda_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  pararnn_status rc = check_problem(pb);
+  if (rc) return rc;
+  if (problem_N(pb) == 0) return PARARNN_OK;
+  if (!s || !g || !d_pre || !aligned(s, 8) || !aligned(g, 8) || !aligned(d_pre, 8)) return PARARNN_ERR_INVALID_ARG;
+  if ((lambda_out && !aligned(lambda_out, 8)) || (d_s0 && !aligned(d_s0, 8))) return PARARNN_ERR_INVALID_ARG;
+  const VjpEntry ve = pick_vjp(pb->cell, pb->pre_dtype);
+  if (!ws || !aligned(ws, 256) || ws_bytes < ve.ws(pb)) return PARARNN_ERR_WORKSPACE;
+  return ve.run(pb, s, g, d_pre, d_w, d_bias, d_s0, lambda_out, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

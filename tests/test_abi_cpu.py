@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every function the
+header declares, the Python binding's struct layouts match the header, and argument validation
+returns the documented status codes before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from nonlinear_rnn_solve_amd import api, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pararnn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.library_path()):
+        build.build(verbose=False)
+    return api.load_library()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|pararnn_status|const char\*|int)\s+(pararnn_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (pararnn_\w+)", out))
+    assert exported == set(names)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0), sizeof(pararnn_newton_opts),'
+                   ' offsetof(pararnn_newton_opts, final_residual), sizeof(pararnn_report),'
+                   ' offsetof(pararnn_report, residual)); return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
+            ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, ctypes.sizeof(api._Report),
+            api._Report.residual.offset]
+    assert got == want
+
+
+def _problem(cell=1, dtype=0, B=2, T=100, D=64, ptr=4096):
+    p = api._Problem()
+    p.cell, p.pre_dtype, p.B, p.T, p.D = cell, dtype, B, T, D
+    for i in range(4):
+        p.pre[i] = ptr
+    p.w = p.bias = ptr
+    p.s0 = None
+    return p
+
+
+def test_workspace_queries(lib):
+    p = _problem()
+    n1 = lib.pararnn_newton_workspace_bytes(ctypes.byref(p), None)
+    p.T = 100000
+    n2 = lib.pararnn_newton_workspace_bytes(ctypes.byref(p), None)
+    assert 0 < n1 < n2
+    assert lib.pararnn_scan_workspace_bytes(1, 8, 16384, 1024) > 0
+    assert lib.pararnn_scan_workspace_bytes(3, 8, 16384, 1024) == 0
+    assert lib.pararnn_vjp_workspace_bytes(ctypes.byref(_problem(cell=2))) > 0
+    p.D = 0
+    assert lib.pararnn_newton_workspace_bytes(ctypes.byref(p), None) == 4096   # empty problem: header only
+
+
+def test_validation_codes_without_launching(lib):
+    opts = api._Opts(3, 0.0, None, 0)
+    ws = ctypes.c_void_p(1 << 20)
+    out = ctypes.c_void_p(4096)
+    solve = lambda p, o=opts, w=ws, n=1 << 40: lib.pararnn_newton_solve(  # noqa: E731
+        ctypes.byref(p), ctypes.byref(o), out, w, n, None, None)
+    assert lib.pararnn_newton_solve(None, ctypes.byref(opts), out, ws, 1 << 40, None, None) == -1
+    assert solve(_problem(cell=7)) == -1
+    assert solve(_problem(dtype=5)) == -1
+    assert solve(_problem(B=-1)) == -1
+    assert solve(_problem(D=63)) == -2                      # odd D is not built
+    p = _problem()
+    p.pre[1] = None
+    assert solve(p) == -1
+    p = _problem()
+    p.pre[0] = 4097                                         # misaligned
+    assert solve(p) == -1
+    assert solve(_problem(), o=api._Opts(0, 0.0, None, 0)) == -1
+    assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
+    assert solve(_problem(), w=ctypes.c_void_p(0)) == -3
+    assert solve(_problem(), w=ctypes.c_void_p(4096 + 8)) == -3   # not 256-byte aligned
+    assert solve(_problem(), n=16) == -3
+    assert solve(_problem(T=0)) == 0                        # empty problem: no-op
+    scan = lambda S, dt, a=4096, n=1 << 40: lib.pararnn_linear_scan(  # noqa: E731
+        S, 8, 100, 64, dt, ctypes.c_void_p(a), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 0,
+        ctypes.c_void_p(1 << 20), n, None)
+    assert scan(3, 0) == -1
+    assert scan(1, 9) == -1
+    assert scan(1, 0, a=0) == -1
+    assert scan(1, 0, n=8) == -3
+    vjp = lambda p: lib.pararnn_scan_vjp(ctypes.byref(p), None, ctypes.c_void_p(4096),  # noqa: E731
+                                         ctypes.c_void_p(4096), None, None, None, None, ws, 1 << 40, None)
+    assert vjp(_problem()) == -1                            # trajectory missing
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.pararnn_status_string(s).decode() != "unknown status"
+    assert lib.pararnn_abi_version() == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    a = torch.zeros(1, 8, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.linear_scan(a, a)
