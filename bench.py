@@ -1,0 +1,212 @@
+"""Benchmark of the ParaRNN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of seeded synthetic input, with the
+inputs already resident in HBM.  Default workload: the long-context diagonal GRU (bf16 storage,
+fp32 arithmetic, B=1, T=131072, D=1024): a Newton solve from the zero guess until the max
+residual is below 1e-5 (at most 8 iterations), then the reverse-scan VJP for an upstream gradient
+dL/dh ~ N(0, 1).  Other workloads (--workload 0..3) time one Newton solve or one linear scan.
+
+Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
+iterations the solve ran (a linear scan counts K = 1).  roofline: the steady-state fused Newton
+iteration kernel (or the scan kernel), algorithmic bytes per element x elements / its mean
+launch duration from HIP events on the launch stream.  cpu_baseline: the fp64 CPU oracle on a
+bounded sample of channels of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "channel-tokens/s per Newton solve (B*T*D*K/s) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+# algorithmic HBM bytes per element of one launch of the dominant kernel
+#   GRU steady iteration: read U (3 planes) + read H^k + write H^{k+1}
+#   LSTM steady iteration: read U (4 planes) + read (c, h)^k + write (c, h)^{k+1}
+#   linear scan: read a, b + write h
+def algo_bytes(cell: str, dtype: str) -> int:
+    esz = 2 if dtype == "bf16" else 4
+    if cell == "gru":
+        return 3 * esz + 4 + 4
+    if cell == "lstm":
+        return 4 * esz + 8 + 8
+    return 2 * esz + 4
+
+
+def vjp_bytes(cell: str, dtype: str) -> int:
+    """VJP kernel: read U, H, g; write dU (fp32, G planes)."""
+    esz = 2 if dtype == "bf16" else 4
+    G, S = {"gru": (3, 1), "lstm": (4, 2), "linear": (2, 1)}[cell]
+    return G * esz + 4 * S + 4 + 4 * G
+
+
+def cpu_threads() -> int:
+    n = os.cpu_count() or 1
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, min(n, 16))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-channels", type=int, default=0, help="channels in the CPU-baseline sample (0: auto)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported (the hot path shards "
+              "without communication, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from nonlinear_rnn_solve_amd import api, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.workload_inputs(wl)
+    if wl.dtype == "bf16":
+        pre = [torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).to(dev) for p in inp.pre]
+    else:
+        pre = [torch.from_numpy(p).to(dev) for p in inp.pre]
+    w = torch.from_numpy(inp.w).to(dev) if inp.w is not None else None
+    b = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    g = torch.from_numpy(inp.g).to(dev) if inp.g is not None else None
+    N = wl.B * wl.T * wl.D
+    out = torch.empty((inp.S, wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    if wl.cell == "linear":
+        out = out[0]
+
+    stream = torch.cuda.current_stream(dev)
+    iter_events = []     # per step: list of (k, start, end)
+
+    def hook(k, phase, rec):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        if phase == "before":
+            rec.append([k, ev, None])
+        else:
+            rec[-1][2] = ev
+
+    vjp_events = []
+
+    def step(record):
+        rec = []
+        if wl.cell == "linear":
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            api.linear_scan(pre[0], pre[1], out=out)
+            e1.record(stream)
+            rec.append([0, e0, e1])
+            iters = 1
+        else:
+            _, rep = api.newton_solve(wl.cell, pre, w, b, max_iters=wl.max_iters, tol=wl.tol, out=out,
+                                      on_iteration=lambda k, ph: hook(k, ph, rec))
+            iters = rep.iters
+            if wl.vjp:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                api.scan_vjp(wl.cell, pre, out, g, w, b, want_s0=False)
+                e1.record(stream)
+                if record:
+                    vjp_events.append((e0, e1))
+        if record:
+            iter_events.append(rec)
+        return iters
+
+    for _ in range(args.warmup):
+        iters = step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        iters = step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # dominant kernel: the steady-state fused Newton iteration (k >= 1 and doing work), or the scan
+    durs = []
+    for rec in iter_events:
+        for k, e0, e1 in rec:
+            if wl.cell == "linear" or (1 <= k < iters):
+                durs.append(e0.elapsed_time(e1))
+    if not durs:  # a solve of one iteration: only the zero-guess launch exists
+        durs = [e0.elapsed_time(e1) for rec in iter_events for k, e0, e1 in rec if k < iters]
+    kern_ms = float(np.mean(durs))
+    per_elem = algo_bytes(wl.cell, wl.dtype)
+    achieved = per_elem * N / (kern_ms * 1e-3) / 1e9
+    value = N * iters / (ms_per_step * 1e-3)
+    kernel_name = "k_tile<LinearOp>" if wl.cell == "linear" else "k_tile<NewtonOp> (iterations k>=1)"
+    line = {
+        "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "cell": wl.cell, "B": wl.B, "T": wl.T, "D": wl.D, "storage": wl.dtype,
+                   "tol": wl.tol, "max_iters": wl.max_iters, "iters": iters, "vjp": wl.vjp},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel_name,
+                     "bytes_per_elem": per_elem, "kernel_ms": kern_ms},
+    }
+    if vjp_events:
+        vms = float(np.mean([a.elapsed_time(b2) for a, b2 in vjp_events]))
+        line["vjp"] = {"ms": vms, "bytes_per_elem": vjp_bytes(wl.cell, wl.dtype),
+                       "gbs": vjp_bytes(wl.cell, wl.dtype) * N / (vms * 1e-3) / 1e9}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inp, iters, args.cpu_channels)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, inp, iters, n_channels):
+    """The fp64 oracle (as it stands) on a sample of channels of the same workload, full T."""
+    import oracle
+    threads = cpu_threads()
+    if n_channels <= 0:
+        # about 10-30 s of work: the oracle costs roughly 1e-7 s per element-iteration per thread
+        per_ch = wl.T * (max(iters, 1) + (2 if wl.vjp else 0)) * 2.0e-7
+        n_channels = int(max(threads, min(wl.B * wl.D, 15.0 * threads / per_ch)))
+    rng = np.random.default_rng(0)
+    all_ch = [(b, d) for b in range(wl.B) for d in range(wl.D)]
+    pick = sorted(rng.choice(len(all_ch), size=min(n_channels, len(all_ch)), replace=False))
+    bs = np.array([all_ch[i][0] for i in pick])
+    ds = np.array([all_ch[i][1] for i in pick])
+    pre = [np.ascontiguousarray(p[bs, :, ds].T[None]) for p in inp.pre]
+    dt = oracle.BF16 if wl.dtype == "bf16" else oracle.F32
+    t0 = time.perf_counter()
+    if wl.cell == "linear":
+        oracle.linear_scan(pre[0], pre[1], dtype=dt, nthreads=threads)
+        k = 1
+    else:
+        prob = oracle.Problem(wl.cell, pre, inp.w[:, ds], inp.bias[:, ds], dtype=dt)
+        H, res, k, conv, rc = oracle.newton(prob, wl.max_iters, tol=wl.tol, nthreads=threads)
+        if wl.vjp:
+            oracle.vjp(prob, H, np.ascontiguousarray(inp.g[bs, :, ds].T[None]), want_lambda=False, nthreads=threads)
+    sec = time.perf_counter() - t0
+    n = len(pick) * wl.T
+    return {"value": n * k / sec, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d channels, full T=%d, %s%s; %.1f s" % (
+                len(pick), wl.B * wl.D, wl.T, "linear scan" if wl.cell == "linear" else
+                "Newton (%d iterations)" % k, " + VJP" if wl.vjp else "", sec)}
+
+
+if __name__ == "__main__":
+    main()

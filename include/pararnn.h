@@ -114,6 +114,24 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_n
                                     float* s_out, void* ws, size_t ws_bytes, void* stream,
                                     pararnn_report* report);
 
+/* The same solve in three steps, for callers that time, checkpoint or interleave work between
+ * iterations.  pararnn_newton_solve(...) is exactly: prepare; iterate k = 0 .. max_iters-1;
+ * [final residual]; report.  All share one workspace and stream; `opts` must be the same object
+ * contents in every call of one solve.
+ *   prepare  -- clears the workspace's counters and look-back words (one small kernel).
+ *   iterate  -- launches iteration k (0 <= k < max_iters): one fused kernel reading H^k (init_guess
+ *               for k = 0, else s_out) and writing H^{k+1} into s_out.  In tolerance mode a kernel
+ *               whose earlier residual met the stop rule exits at once without touching s_out.
+ *   report   -- (host) optionally launches the final-residual pass, waits for the stream and fills
+ *               `report`; returns DIVERGED as pararnn_newton_solve does.                              */
+pararnn_status pararnn_newton_prepare(const pararnn_problem* prob, const pararnn_newton_opts* opts,
+                                      void* ws, size_t ws_bytes, void* stream);
+pararnn_status pararnn_newton_iterate(const pararnn_problem* prob, const pararnn_newton_opts* opts,
+                                      int k, float* s_out, void* ws, size_t ws_bytes, void* stream);
+pararnn_status pararnn_newton_report(const pararnn_problem* prob, const pararnn_newton_opts* opts,
+                                     const float* s_out, void* ws, size_t ws_bytes, void* stream,
+                                     pararnn_report* report);
+
 /* ------------------------------------------------------------------------------------------------
  * pararnn_linear_scan -- the linear recurrence every Newton step reduces to (pararnn-torch README,
  * "Method": each linear solve is an associative scan over time), as a single-pass parallel scan.

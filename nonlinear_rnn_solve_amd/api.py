@@ -90,6 +90,12 @@ def load_library():
     lib.pararnn_newton_workspace_bytes.argtypes = [vp, vp]
     lib.pararnn_newton_solve.restype = i32
     lib.pararnn_newton_solve.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    lib.pararnn_newton_prepare.restype = i32
+    lib.pararnn_newton_prepare.argtypes = [vp, vp, vp, sz, vp]
+    lib.pararnn_newton_iterate.restype = i32
+    lib.pararnn_newton_iterate.argtypes = [vp, vp, i32, vp, vp, sz, vp]
+    lib.pararnn_newton_report.restype = i32
+    lib.pararnn_newton_report.argtypes = [vp, vp, vp, vp, sz, vp, vp]
     lib.pararnn_scan_workspace_bytes.restype = sz
     lib.pararnn_scan_workspace_bytes.argtypes = [i32, i64, i64, i64]
     lib.pararnn_linear_scan.restype = i32
@@ -174,12 +180,15 @@ def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
 
 
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
-                 final_residual=False, report=True):
+                 final_residual=False, report=True, on_iteration=None):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
     tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
     (evaluated at its input iterate) is below tol.  report=True waits for the stream.
+    on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
+    launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
+    entry points prepare / iterate / report, which launch exactly the same kernels.
     """
     lib = load_library()
     st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0)
@@ -197,8 +206,22 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
     ws = _workspace(nbytes, dev, "newton")
     rep = _Report() if report else None
-    rc = lib.pararnn_newton_solve(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
-                                  _stream(dev), ctypes.byref(rep) if rep is not None else None)
+    stream = _stream(dev)
+    if on_iteration is None:
+        rc = lib.pararnn_newton_solve(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
+                                      stream, ctypes.byref(rep) if rep is not None else None)
+    else:
+        rc = lib.pararnn_newton_prepare(ctypes.byref(st), ctypes.byref(opts), _ptr(ws), ws.numel(), stream)
+        for k in range(int(max_iters)):
+            if rc != 0:
+                break
+            on_iteration(k, "before")
+            rc = lib.pararnn_newton_iterate(ctypes.byref(st), ctypes.byref(opts), k, _ptr(out), _ptr(ws),
+                                            ws.numel(), stream)
+            on_iteration(k, "after")
+        if rc == 0:
+            rc = lib.pararnn_newton_report(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
+                                           stream, ctypes.byref(rep) if rep is not None else None)
     r = None
     if rep is not None:
         res = [float(rep.residual[i]) for i in range(rep.n_residual)]

@@ -193,8 +193,13 @@ struct Common {
 struct Tile {
   int64_t p, chunk, t_lo, ch0, b, d0;
   int chain, wave, lane;
+  int nvalid;   // steps of this lane inside [0, T); the same for every lane of the wave
   bool active;
 };
+
+// row of step t clamped into [0, T): loads use clamped addresses and masked steps are replaced by
+// identity elements afterwards, so the load phase has no branches and every load is in flight at once
+DEV int64_t clamp_t(int64_t t, int64_t T) { return t < 0 ? 0 : (t >= T ? T - 1 : t); }
 
 template <int S, int TW, int NSLOT>
 DEV uint64_t* word_at(const Common& c, int64_t p, int chain, int slot, int q) {
@@ -273,7 +278,8 @@ DEV float wave_nanmax(float m) {
 // the generic tile kernel
 // ------------------------------------------------------------------------------------------------
 template <class Op>
-__global__ __launch_bounds__(Op::NW * WAVE) void k_tile(const typename Op::Args a) {
+__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(Op::MINW)))
+void k_tile(const typename Op::Args a) {
   constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TW = WAVE * V, NA = S * S + S;
   constexpr int NSLOT = Op::NSLOT;
   constexpr bool REV = Op::REVERSE;
@@ -298,6 +304,10 @@ __global__ __launch_bounds__(Op::NW * WAVE) void k_tile(const typename Op::Args 
   tl.active = tl.ch0 < c.C;
   tl.b = tl.active ? tl.ch0 / c.D : 0;
   tl.d0 = tl.active ? tl.ch0 - tl.b * c.D : 0;
+  {
+    const int64_t left = c.T - tl.t_lo;
+    tl.nvalid = static_cast<int>(left < 0 ? 0 : (left > L ? L : left));
+  }
 
   typename Op::Lane ln;
   float rmax = Op::produce(a, tl, ln);
@@ -405,19 +415,59 @@ template <> struct CellInfo<CELL_LINEAR> { static constexpr int S = 1, G = 2; };
 template <> struct CellInfo<CELL_GRU> { static constexpr int S = 1, G = 3; };
 template <> struct CellInfo<CELL_LSTM> { static constexpr int S = 2, G = 4; };
 
+// Per-lane channel parameters for V channels: the recurrent weights w and biases b, and the same
+// two scaled by the exponent factor of their gate (-log2(e) for a sigmoid gate, 2 log2(e) for a tanh
+// gate), so that a gate's exp2 argument is fma(sw, h, fma(scale, U, sb)) = scale * (U + w h + b).
+template <int G, int V>
+struct Params {
+  float w[G][V], bias[G][V], sw[G][V], sb[G][V];
+};
+template <int CELL> DEV float gate_scale(int g);
+template <> DEV float gate_scale<CELL_GRU>(int g) { return g == 2 ? 2.0f * kLog2e : -kLog2e; }     // z, r, c
+template <> DEV float gate_scale<CELL_LSTM>(int g) { return g == 3 ? 2.0f * kLog2e : -kLog2e; }    // i, f, o, g
+template <> DEV float gate_scale<CELL_LINEAR>(int) { return 0.0f; }
+
+template <int CELL, int G, int V>
+DEV void load_params(const float* w, const float* bias, int64_t D, int64_t d0, Params<G, V>& pm) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    ldv<V, DT_F32>(w, g * D + d0, pm.w[g]);
+    ldv<V, DT_F32>(bias, g * D + d0, pm.bias[g]);
+    const float sc = gate_scale<CELL>(g);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      pm.sw[g][v] = sc * pm.w[g][v];
+      pm.sb[g][v] = sc * pm.bias[g][v];
+    }
+  }
+}
+
+// sigmoid and tanh of a pre-scaled exponent argument x (see Params)
+DEV float sig_x(float x) { return hw_rcp(1.0f + hw_exp2(x)); }
+DEV float tanh_x(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(x)), 1.0f); }
+
 // GRU: z = sig(U_z + a_z h + b_z), r = sig(U_r + a_r h + b_r), c = tanh(U_c + a_c r h + b_c),
 //      h' = (1 - z) h + z c,  J = (1 - z) + (c - h) z (1 - z) a_z + z (1 - c^2) a_c (r + h r (1 - r) a_r)
-DEV void gru_eval(float uz, float ur, float uc, float az, float ar, float ac, float bz, float br,
-                  float bc, float h, float& f, float& J) {
-  const float z = sigmoid(fmaf(az, h, uz + bz));
-  const float r = sigmoid(fmaf(ar, h, ur + br));
-  const float c = tanh_(fmaf(ac, r * h, uc + bc));
+//      gate partials: d h'/d u_z = (c - h) z (1 - z), d h'/d u_c = z (1 - c^2),
+//                     d h'/d u_r = d h'/d u_c a_c h r (1 - r)
+struct GruOut {
+  float f, J, pz, pc, r;
+};
+template <int G, int V>
+DEV GruOut gru_eval(const Params<G, V>& pm, int v, float uz, float ur, float uc, float h) {
+  GruOut o;
+  const float z = sig_x(fmaf(pm.sw[0][v], h, fmaf(-kLog2e, uz, pm.sb[0][v])));
+  const float r = sig_x(fmaf(pm.sw[1][v], h, fmaf(-kLog2e, ur, pm.sb[1][v])));
+  const float c = tanh_x(fmaf(pm.sw[2][v], r * h, fmaf(2.0f * kLog2e, uc, pm.sb[2][v])));
   const float cmh = c - h;
-  f = fmaf(z, cmh, h);
-  const float zz = z * (1.0f - z);
-  const float dc = z * fmaf(-c, c, 1.0f);                // z (1 - c^2)
-  const float rr = r * (1.0f - r);
-  J = fmaf(dc * ac, fmaf(h * rr, ar, r), fmaf(cmh * zz, az, 1.0f - z));
+  o.f = fmaf(z, cmh, h);
+  const float zz = fmaf(-z, z, z);                    // z (1 - z)
+  const float rr = fmaf(-r, r, r);                    // r (1 - r)
+  o.pc = z * fmaf(-c, c, 1.0f);                       // z (1 - c^2)
+  o.pz = cmh * zz;
+  o.r = r;
+  o.J = fmaf(o.pc * pm.w[2][v], fmaf(h * rr, pm.w[1][v], r), fmaf(o.pz, pm.w[0][v], 1.0f - z));
+  return o;
 }
 
 // LSTM: i, f, o = sig(U + w h + b), g = tanh(U_g + w_g h + b_g), c' = f c + i g, h' = o tanh(c')
@@ -427,42 +477,39 @@ struct LstmPart {
   float dc_i, dc_f, dc_g; // d c' / d u_{i,f,g}
   float dh_o, kh;         // d h' / d u_o, d h' / d c'
 };
-DEV LstmPart lstm_eval(float ui, float uf, float uo, float ug, float wi, float wf, float wo,
-                       float wg, float bi, float bf, float bo, float bg, float c, float h) {
+template <int G, int V>
+DEV LstmPart lstm_eval(const Params<G, V>& pm, int v, float ui, float uf, float uo, float ug, float c, float h) {
   LstmPart p;
-  const float ig = sigmoid(fmaf(wi, h, ui + bi));
-  const float fg = sigmoid(fmaf(wf, h, uf + bf));
-  const float og = sigmoid(fmaf(wo, h, uo + bo));
-  const float gg = tanh_(fmaf(wg, h, ug + bg));
+  const float ig = sig_x(fmaf(pm.sw[0][v], h, fmaf(-kLog2e, ui, pm.sb[0][v])));
+  const float fg = sig_x(fmaf(pm.sw[1][v], h, fmaf(-kLog2e, uf, pm.sb[1][v])));
+  const float og = sig_x(fmaf(pm.sw[2][v], h, fmaf(-kLog2e, uo, pm.sb[2][v])));
+  const float gg = tanh_x(fmaf(pm.sw[3][v], h, fmaf(2.0f * kLog2e, ug, pm.sb[3][v])));
   p.c2 = fmaf(fg, c, ig * gg);
-  const float tc = tanh_(p.c2);
+  const float tc = tanh_x(2.0f * kLog2e * p.c2);
   p.h2 = og * tc;
-  p.dc_i = gg * ig * (1.0f - ig);
-  p.dc_f = c * fg * (1.0f - fg);
+  p.dc_i = gg * fmaf(-ig, ig, ig);
+  p.dc_f = c * fmaf(-fg, fg, fg);
   p.dc_g = ig * fmaf(-gg, gg, 1.0f);
   p.kh = og * fmaf(-tc, tc, 1.0f);
-  p.dh_o = tc * og * (1.0f - og);
-  const float dc_dh = fmaf(p.dc_i, wi, fmaf(p.dc_f, wf, p.dc_g * wg));
+  p.dh_o = tc * fmaf(-og, og, og);
+  const float dc_dh = fmaf(p.dc_i, pm.w[0][v], fmaf(p.dc_f, pm.w[1][v], p.dc_g * pm.w[3][v]));
   p.J00 = fg;
   p.J01 = dc_dh;
   p.J10 = p.kh * fg;
-  p.J11 = fmaf(p.dh_o, wo, p.kh * dc_dh);
+  p.J11 = fmaf(p.dh_o, pm.w[2][v], p.kh * dc_dh);
   return p;
 }
 
-// per-lane channel parameters (w, bias) for V channels
-template <int G, int V>
-struct Params {
-  float w[G][V], bias[G][V];
-};
-template <int G, int V>
-DEV void load_params(const float* w, const float* bias, int64_t D, int64_t d0, Params<G, V>& pm) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    ldv<V, DT_F32>(w, g * D + d0, pm.w[g]);
-    ldv<V, DT_F32>(bias, g * D + d0, pm.bias[g]);
+// running max of |r| that is cheap per step; a NaN or an infinity is caught by bad = fma(r, 0, bad)
+// (NaN iff some r was NaN or infinite), and folded into the result at the end
+struct ResidMax {
+  float m = 0.0f, bad = 0.0f;
+  DEV void add(float r) {
+    m = __builtin_fmaxf(m, fabsf(r));
+    bad = fmaf(r, 0.0f, bad);
   }
-}
+  DEV float get() const { return bad == bad ? m : __builtin_nanf(""); }
+};
 
 template <int S, int V>
 DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&x)[V][S]) {
@@ -483,9 +530,9 @@ DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&
 // ------------------------------------------------------------------------------------------------
 // Op 1: linear recurrence (pararnn_linear_scan)
 // ------------------------------------------------------------------------------------------------
-template <int S_, int DT, bool REV, int V_, int L_, int NW_>
+template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_>
 struct LinearOp {
-  static constexpr int S = S_, V = V_, L = L_, NW = NW_;
+  static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_;
   static constexpr bool REVERSE = REV, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
@@ -505,45 +552,38 @@ struct LinearOp {
   static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
     load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
   }
+  // Lanes past the last channel load channel 0 (valid addresses) and are never published or
+  // stored; steps past T use clamped addresses and become identity elements (MASKED path only).
   static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
-    const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
+    if (tl.nvalid == L) produce_t<false>(a, tl, ln);
+    else produce_t<true>(a, tl, ln);
+    return 0.0f;
+  }
+  template <bool MASKED>
+  static DEV void produce_t(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
+    float av[S * S][L][V], bv[S][L][V];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const bool ok = tl.active && (tl.t_lo + i < a.c.T);
-      const int64_t idx = base + i * a.c.D;
-      if constexpr (S == 1) {
-        float av[V], bv[V];
-        if (ok) {
-          ldv<V, DT>(a.a, idx, av);
-          ldv<V, DT>(a.b, idx, bv);
-        }
+      const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
+      const int64_t idx = (row + t) * D + tl.d0;
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          ln.e[v][i].A[0] = ok ? av[v] : 1.0f;
-          ln.e[v][i].b[0] = ok ? bv[v] : 0.0f;
-        }
-      } else {
-        float av[4][V], bv[2][V];
-        if (ok) {
+      for (int k = 0; k < S * S; ++k) ldv<V, DT>(a.a, k * N + idx, av[k][i]);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) ldv<V, DT>(a.a, k * a.c.N + idx, av[k]);
+      for (int k = 0; k < S; ++k) ldv<V, DT>(a.b, k * N + idx, bv[k][i]);
+    }
 #pragma unroll
-          for (int k = 0; k < 2; ++k) ldv<V, DT>(a.b, k * a.c.N + idx, bv[k]);
-        }
+    for (int i = 0; i < L; ++i) {
+      const bool ok = !MASKED || i < tl.nvalid;
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          if (ok) {
+      for (int v = 0; v < V; ++v) {
+        const Aff<S> one = aff_id<S>();
 #pragma unroll
-            for (int k = 0; k < 4; ++k) ln.e[v][i].A[k] = av[k][v];
+        for (int k = 0; k < S * S; ++k) ln.e[v][i].A[k] = ok ? av[k][i][v] : one.A[k];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) ln.e[v][i].b[k] = bv[k][v];
-          } else {
-            ln.e[v][i] = aff_id<S>();
-          }
-        }
+        for (int k = 0; k < S; ++k) ln.e[v][i].b[k] = ok ? bv[k][i][v] : 0.0f;
       }
     }
-    return 0.0f;
   }
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
     if (!tl.active) return;
@@ -551,7 +591,7 @@ struct LinearOp {
 #pragma unroll
     for (int s = 0; s < L; ++s) {
       const int i = REV ? L - 1 - s : s;
-      if (tl.t_lo + i >= a.c.T) continue;
+      if (i >= tl.nvalid) continue;
 #pragma unroll
       for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
 #pragma unroll
@@ -572,10 +612,10 @@ struct LinearOp {
 //   r_t = h^k_t - f_t (the same iterate, written without forming delta).  The max |r_t| is
 //   reduced for the tolerance test.  LINEAR: the element is (a_t, b_t) itself.
 // ------------------------------------------------------------------------------------------------
-template <int CELL, int DT, int V_, int L_, int NW_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_>
 struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
-  static constexpr int V = V_, L = L_, NW = NW_;
+  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_;
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
@@ -609,50 +649,48 @@ struct NewtonOp {
     load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
   }
   static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
-    float rmax = 0.0f;
-    const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
+    return tl.nvalid == L ? produce_t<false>(a, tl, ln) : produce_t<true>(a, tl, ln);
+  }
+  template <bool MASKED>
+  static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
     const Common& c = a.c;
     constexpr int TW = WAVE * V;
     const int q0 = tl.lane * V;
-    if (!tl.active) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int i = 0; i < L; ++i) ln.e[v][i] = aff_id<S>();
-      return 0.0f;
-    }
-    const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
-    // current iterate at steps t_lo-1 .. t_lo+L-1 (index 0 is the step before the lane's first)
-    float h[S][L + 1][V];
     const bool have_h = a.h_in != nullptr;
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const bool ok = tl.t_lo + i < T;
-#pragma unroll
-      for (int k = 0; k < S; ++k) {
-        if (have_h && ok) {
-          ldv<V, DT_F32>(a.h_in, k * N + base + i * D, h[k][i + 1]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < V; ++v) h[k][i + 1][v] = 0.0f;
-        }
-      }
-    }
+    // loads first, all of them: the current iterate at steps t_lo-1 .. t_lo+L-1 (h[.][0] is the
+    // step before the lane's first) and the gate inputs of the lane's L steps
+    float h[S][L + 1][V];
     float u[G][L][V];
+    if (have_h) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
+#pragma unroll
+        for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.h_in, k * N + (row + t) * D + tl.d0, h[k][i + 1]);
+      }
+      if (tl.wave != 0) {
+        // h^k_{t_lo-1} lies in this tile's chunk (written only after the tile's look-back)
+        const int64_t idx = (row + clamp_t(tl.t_lo - 1, T)) * D + tl.d0;
+#pragma unroll
+        for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.h_in, k * N + idx, h[k][0]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i <= L; ++i)
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+#pragma unroll
+          for (int v = 0; v < V; ++v) h[k][i][v] = 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const bool ok = tl.t_lo + i < T;
+      const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (ok) {
-          ldv<V, DT>(a.pre[g], base + i * D, u[g][i]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < V; ++v) u[g][i][v] = 0.0f;
-        }
-      }
+      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], (row + t) * D + tl.d0, u[g][i]);
     }
-    // the state before the lane's first step
+    Params<G, V> pm;
+    if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(a.w, a.bias, D, tl.d0, pm);
     if (tl.t_lo == 0) {
       float x[V][S];
       load_s0<S, V>(a.s0, a.B, D, tl, x);
@@ -660,28 +698,11 @@ struct NewtonOp {
       for (int k = 0; k < S; ++k)
 #pragma unroll
         for (int v = 0; v < V; ++v) h[k][0][v] = x[v][k];
-    } else if (!have_h) {
-#pragma unroll
-      for (int k = 0; k < S; ++k)
-#pragma unroll
-        for (int v = 0; v < V; ++v) h[k][0][v] = 0.0f;
-    } else if (tl.wave != 0) {
-      // h^k_{t_lo-1} lies in this tile (written only after the tile's look-back); a lane whose
-      // steps all lie past T reads nothing
-#pragma unroll
-      for (int k = 0; k < S; ++k) {
-        if (tl.t_lo <= T) {
-          ldv<V, DT_F32>(a.h_in, k * N + base - D, h[k][0]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < V; ++v) h[k][0][v] = 0.0f;
-        }
-      }
     }
-    if (have_h) {
+    if (have_h && tl.active) {
       // publish this tile's last state (the h^k the next tile's first step needs), then take the
       // previous tile's: the trajectory is updated in place, so it cannot be re-read from memory
-      if (tl.wave == NW - 1 && tl.t_lo + L - 1 < T && tl.p + 1 < c.n_chunks) {
+      if (tl.wave == NW - 1 && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -703,53 +724,54 @@ struct NewtonOp {
           }
       }
     }
-    Params<G, V> pm;
-    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(a.w, a.bias, D, tl.d0, pm);
+    ResidMax rm;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const bool ok = tl.t_lo + i < T;
+      const bool ok = !MASKED || i < tl.nvalid;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        if (!ok) {
-          ln.e[v][i] = aff_id<S>();
-          continue;
-        }
+        Aff<S> e;
         if constexpr (CELL == CELL_LINEAR) {
-          const float hp = h[0][i][v];
-          const float f = fmaf(u[0][i][v], hp, u[1][i][v]);
-          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - f));
-          ln.e[v][i].A[0] = u[0][i][v];
-          ln.e[v][i].b[0] = u[1][i][v];
+          const float f = fmaf(u[0][i][v], h[0][i][v], u[1][i][v]);
+          if (ok) rm.add(h[0][i + 1][v] - f);
+          e.A[0] = u[0][i][v];
+          e.b[0] = u[1][i][v];
         } else if constexpr (CELL == CELL_GRU) {
           const float hp = h[0][i][v];
-          float f, J;
-          gru_eval(u[0][i][v], u[1][i][v], u[2][i][v], pm.w[0][v], pm.w[1][v], pm.w[2][v],
-                   pm.bias[0][v], pm.bias[1][v], pm.bias[2][v], hp, f, J);
-          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - f));
-          ln.e[v][i].A[0] = J;
-          ln.e[v][i].b[0] = fmaf(-J, hp, f);
+          const GruOut q = gru_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], hp);
+          if (ok) rm.add(h[0][i + 1][v] - q.f);
+          e.A[0] = q.J;
+          e.b[0] = fmaf(-q.J, hp, q.f);
         } else {
           const float cp = h[0][i][v], hp = h[1][i][v];
-          const LstmPart q = lstm_eval(u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], pm.w[0][v],
-                                       pm.w[1][v], pm.w[2][v], pm.w[3][v], pm.bias[0][v],
-                                       pm.bias[1][v], pm.bias[2][v], pm.bias[3][v], cp, hp);
-          rmax = nanmax(rmax, fabsf(h[0][i + 1][v] - q.c2));
-          rmax = nanmax(rmax, fabsf(h[1][i + 1][v] - q.h2));
-          Aff<2>& e = ln.e[v][i];
+          const LstmPart q = lstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], cp, hp);
+          if (ok) {
+            rm.add(h[0][i + 1][v] - q.c2);
+            rm.add(h[1][i + 1][v] - q.h2);
+          }
           e.A[0] = q.J00; e.A[1] = q.J01; e.A[2] = q.J10; e.A[3] = q.J11;
           e.b[0] = q.c2 - fmaf(q.J00, cp, q.J01 * hp);
           e.b[1] = q.h2 - fmaf(q.J10, cp, q.J11 * hp);
         }
+        if (MASKED) {
+          const Aff<S> one = aff_id<S>();
+#pragma unroll
+          for (int k = 0; k < S * S; ++k) ln.e[v][i].A[k] = ok ? e.A[k] : one.A[k];
+#pragma unroll
+          for (int k = 0; k < S; ++k) ln.e[v][i].b[k] = ok ? e.b[k] : 0.0f;
+        } else {
+          ln.e[v][i] = e;
+        }
       }
     }
-    return rmax;
+    return tl.active ? rm.get() : 0.0f;
   }
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
     if (!tl.active) return;
     const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      if (tl.t_lo + i >= a.c.T) continue;
+      if (i >= tl.nvalid) continue;
 #pragma unroll
       for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
 #pragma unroll
@@ -773,10 +795,10 @@ template <> struct VjpStash<CELL_LINEAR> { float hp; };
 template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
 template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
 
-template <int CELL, int DT, int V_, int L_, int NW_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_>
 struct VjpOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
-  static constexpr int V = V_, L = L_, NW = NW_;
+  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_;
   static constexpr bool REVERSE = true, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
@@ -800,6 +822,7 @@ struct VjpOp {
     Aff<S> e[V][L];
     VjpStash<CELL> st[V][L];
     float J0[V][S * S];   // Jacobian at step 0 (only used by the lane that owns t = 0)
+    float ac[V];          // GRU: a_c, for d h'/d u_r
   };
   static DEV bool skip(const Args&) { return false; }
   static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
@@ -809,107 +832,96 @@ struct VjpOp {
       for (int k = 0; k < S; ++k) x[v][k] = 0.0f;   // nothing flows in from beyond the last step
   }
   static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
-    const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
+    // the unmasked path needs every step and the next lane's first step inside [0, T)
+    if (tl.t_lo + L < a.c.T) produce_t<false>(a, tl, ln);
+    else produce_t<true>(a, tl, ln);
+    return 0.0f;
+  }
+  template <bool MASKED>
+  static DEV void produce_t(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
+    // loads first: evaluation e (0..L) is the cell step at t = t_lo + e, which needs U_t and
+    // s_{t-1}; e = L belongs to the next lane's first step and only contributes its Jacobian
+    float u[G][L + 1][V], sp[S][L + 1][V], gv[L][V];
+#pragma unroll
+    for (int e = 0; e <= L; ++e) {
+      const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
+      const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
+#pragma unroll
+      for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
+      if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
+    }
+    if (tl.t_lo == 0) {
+      float x[V][S];
+      load_s0<S, V>(a.s0, a.B, D, tl, x);
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) sp[k][0][v] = x[v][k];
+    }
+    Params<G, V> pm;
+    if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(a.w, a.bias, D, tl.d0, pm);
+    if constexpr (CELL == CELL_GRU) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) ln.ac[v] = pm.w[2][v];
+    }
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int k = 0; k < S * S; ++k) ln.J0[v][k] = 0.0f;
-    if (!tl.active) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int i = 0; i < L; ++i) ln.e[v][i] = aff_id<S>();
-      return 0.0f;
-    }
-    const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
-    Params<G, V> pm;
-    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(a.w, a.bias, D, tl.d0, pm);
-    // evaluations e = L .. 0 at time t_lo + e (e = L is the first step of the next lane / chunk)
-    float Jn[V][S * S];   // Jacobian of evaluation e+1, transposed into the element of step e
+    // evaluations e = L .. 0; the element of step e takes the (transposed) Jacobian of e + 1
+    float Jn[V][S * S];
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int k = 0; k < S * S; ++k) Jn[v][k] = 0.0f;
 #pragma unroll
     for (int e = L; e >= 0; --e) {
-      const int64_t t = tl.t_lo + e;
-      const bool ok = t < T;
-      float u[G][V], sp[S][V], gv[V];
-      if (ok) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], base + e * D, u[g]);
-        if (t == 0) {
-          float x[V][S];
-          load_s0<S, V>(a.s0, a.B, D, tl, x);
-#pragma unroll
-          for (int k = 0; k < S; ++k)
-#pragma unroll
-            for (int v = 0; v < V; ++v) sp[k][v] = x[v][k];
-        } else {
-#pragma unroll
-          for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + base + (e - 1) * D, sp[k]);
-        }
-        if (e < L) ldv<V, DT_F32>(a.g, base + e * D, gv);
-      }
+      const bool ok = !MASKED || e < tl.nvalid || (e == L && tl.t_lo + L < T);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         float J[S * S];
-#pragma unroll
-        for (int k = 0; k < S * S; ++k) J[k] = 0.0f;
         VjpStash<CELL> st{};
-        if (ok) {
-          if constexpr (CELL == CELL_LINEAR) {
-            J[0] = u[0][v];
-            st.hp = sp[0][v];
-          } else if constexpr (CELL == CELL_GRU) {
-            const float hp = sp[0][v];
-            const float az = pm.w[0][v], ar = pm.w[1][v], ac = pm.w[2][v];
-            const float z = sigmoid(fmaf(az, hp, u[0][v] + pm.bias[0][v]));
-            const float r = sigmoid(fmaf(ar, hp, u[1][v] + pm.bias[1][v]));
-            const float cc = tanh_(fmaf(ac, r * hp, u[2][v] + pm.bias[2][v]));
-            const float cmh = cc - hp;
-            const float zz = z * (1.0f - z);
-            const float dc = z * fmaf(-cc, cc, 1.0f);
-            const float rr = r * (1.0f - r);
-            J[0] = fmaf(dc * ac, fmaf(hp * rr, ar, r), fmaf(cmh * zz, az, 1.0f - z));
-            st.pz = cmh * zz;
-            st.pc = dc;
-            st.hp = hp;
-            st.r = r;
-          } else {
-            const LstmPart q = lstm_eval(u[0][v], u[1][v], u[2][v], u[3][v], pm.w[0][v], pm.w[1][v],
-                                         pm.w[2][v], pm.w[3][v], pm.bias[0][v], pm.bias[1][v],
-                                         pm.bias[2][v], pm.bias[3][v], sp[0][v], sp[1][v]);
-            J[0] = q.J00; J[1] = q.J01; J[2] = q.J10; J[3] = q.J11;
-            st.dci = q.dc_i; st.dcf = q.dc_f; st.dcg = q.dc_g; st.dho = q.dh_o; st.kh = q.kh;
-            st.hp = sp[1][v];
-          }
+        if constexpr (CELL == CELL_LINEAR) {
+          J[0] = u[0][e][v];
+          st.hp = sp[0][e][v];
+        } else if constexpr (CELL == CELL_GRU) {
+          const GruOut q = gru_eval(pm, v, u[0][e][v], u[1][e][v], u[2][e][v], sp[0][e][v]);
+          J[0] = q.J;
+          st.pz = q.pz;
+          st.pc = q.pc;
+          st.hp = sp[0][e][v];
+          st.r = q.r;
+        } else {
+          const LstmPart q = lstm_eval(pm, v, u[0][e][v], u[1][e][v], u[2][e][v], u[3][e][v], sp[0][e][v],
+                                       sp[1][e][v]);
+          J[0] = q.J00; J[1] = q.J01; J[2] = q.J10; J[3] = q.J11;
+          st.dci = q.dc_i; st.dcf = q.dc_f; st.dcg = q.dc_g; st.dho = q.dh_o; st.kh = q.kh;
+          st.hp = sp[1][e][v];
         }
         if (e < L) {
+          const bool okl = !MASKED || e < tl.nvalid;
           Aff<S>& el = ln.e[v][e];
-          if (ok) {
-            // A = J_{t+1}^T
+          // A = J_{t+1}^T (zero past the last step), b = e_h g_t; identity for masked steps
 #pragma unroll
-            for (int i = 0; i < S; ++i)
+          for (int i = 0; i < S; ++i)
 #pragma unroll
-              for (int j = 0; j < S; ++j) el.A[i * S + j] = Jn[v][j * S + i];
+            for (int j = 0; j < S; ++j) el.A[i * S + j] = okl ? Jn[v][j * S + i] : (i == j ? 1.0f : 0.0f);
 #pragma unroll
-            for (int k = 0; k < S; ++k) el.b[k] = 0.0f;
-            el.b[S - 1] = gv[v];
-            ln.st[v][e] = st;
-            if (t == 0) {
+          for (int k = 0; k < S; ++k) el.b[k] = 0.0f;
+          el.b[S - 1] = okl ? gv[e][v] : 0.0f;
+          ln.st[v][e] = st;
+          if (e == 0 && tl.t_lo == 0) {
 #pragma unroll
-              for (int k = 0; k < S * S; ++k) ln.J0[v][k] = J[k];
-            }
-          } else {
-            el = aff_id<S>();
+            for (int k = 0; k < S * S; ++k) ln.J0[v][k] = J[k];
           }
         }
 #pragma unroll
         for (int k = 0; k < S * S; ++k) Jn[v][k] = ok ? J[k] : 0.0f;
       }
     }
-    return 0.0f;
   }
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
     constexpr int TW = WAVE * V;
@@ -940,7 +952,7 @@ struct VjpOp {
             du[1][v] = x[v][0];
           } else if constexpr (CELL == CELL_GRU) {
             const float l = x[v][0];
-            const float ac = a.w[2 * D + tl.d0 + v];
+            const float ac = ln.ac[v];
             du[0][v] = l * st.pz;
             du[2][v] = l * st.pc;
             du[1][v] = du[2][v] * ac * st.hp * st.r * (1.0f - st.r);
@@ -1011,21 +1023,39 @@ __global__ void k_zero(uint4* p, int64_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// fixed-order reduction of the VJP parameter partials: out[j][d] = sum_b sum_chunk partial[chunk][j][b*D+d]
-__global__ void k_param_reduce(const float* partial, int64_t n_chunks, int npar, int64_t B, int64_t D,
-                               float* d_w, float* d_bias, int G) {
-  const int64_t C = B * D;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= npar * D) return;
-  const int j = static_cast<int>(i / D);
-  const int64_t d = i - j * D;
+// fixed-order reduction of the VJP parameter partials:
+//   out[j][d] = sum over rows r = (b, chunk) of partial[chunk][j][b*D + d]
+// A workgroup owns 64 consecutive outputs; its 16 row groups each add every 16th row, then the 16
+// partial sums are added in row-group order (bitwise reproducible).
+constexpr int kRedCols = 64, kRedRows = 16;
+__global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce(const float* partial, int64_t n_chunks, int npar,
+                                                                     int64_t B, int64_t D, float* d_w, float* d_bias,
+                                                                     int G) {
+  __shared__ float sh[kRedRows][kRedCols];
+  const int col = threadIdx.x % kRedCols, rg = threadIdx.x / kRedCols;
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * kRedCols + col;   // output index j*D + d
+  const int64_t C = B * D, R = B * n_chunks;
   float sum = 0.0f;
-  for (int64_t b = 0; b < B; ++b)
-    for (int64_t ch = 0; ch < n_chunks; ++ch) sum += partial[(ch * npar + j) * C + b * D + d];
-  if (j < G) {
-    if (d_w) d_w[j * D + d] = sum;
-  } else {
-    if (d_bias) d_bias[(j - G) * D + d] = sum;
+  if (o < npar * D) {
+    const int j = static_cast<int>(o / D);
+    const int64_t d = o - j * D;
+    for (int64_t r = rg; r < R; r += kRedRows) {
+      const int64_t b = r / n_chunks, ch = r - b * n_chunks;
+      sum += partial[(ch * npar + j) * C + b * D + d];
+    }
+  }
+  sh[rg][col] = sum;
+  __syncthreads();
+  if (rg == 0 && o < npar * D) {
+    float t = 0.0f;
+    for (int i = 0; i < kRedRows; ++i) t += sh[i][col];
+    const int j = static_cast<int>(o / D);
+    const int64_t d = o - j * D;
+    if (j < G) {
+      if (d_w) d_w[j * D + d] = t;
+    } else {
+      if (d_bias) d_bias[(j - G) * D + d] = t;
+    }
   }
 }
 
@@ -1046,7 +1076,7 @@ __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1
   if (chunk * L < T && col * V < C) {
     const int64_t ch0 = col * V, b = ch0 / D, d0 = ch0 - b * D;
     Params<G, V> pm;
-    if constexpr (CELL != CELL_LINEAR) load_params<G, V>(w, bias, D, d0, pm);
+    if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(w, bias, D, d0, pm);
     for (int i = 0; i < L; ++i) {
       const int64_t t = chunk * L + i;
       if (t >= T) break;
@@ -1071,14 +1101,10 @@ __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1
         if constexpr (CELL == CELL_LINEAR) {
           m = nanmax(m, fabsf(cur[0][v] - fmaf(u[0][v], prev[0][v], u[1][v])));
         } else if constexpr (CELL == CELL_GRU) {
-          float f, J;
-          gru_eval(u[0][v], u[1][v], u[2][v], pm.w[0][v], pm.w[1][v], pm.w[2][v], pm.bias[0][v],
-                   pm.bias[1][v], pm.bias[2][v], prev[0][v], f, J);
-          m = nanmax(m, fabsf(cur[0][v] - f));
+          const GruOut q = gru_eval(pm, v, u[0][v], u[1][v], u[2][v], prev[0][v]);
+          m = nanmax(m, fabsf(cur[0][v] - q.f));
         } else {
-          const LstmPart q = lstm_eval(u[0][v], u[1][v], u[2][v], u[3][v], pm.w[0][v], pm.w[1][v],
-                                       pm.w[2][v], pm.w[3][v], pm.bias[0][v], pm.bias[1][v],
-                                       pm.bias[2][v], pm.bias[3][v], prev[0][v], prev[1][v]);
+          const LstmPart q = lstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], prev[0][v], prev[1][v]);
           m = nanmax(m, fabsf(cur[0][v] - q.c2));
           m = nanmax(m, fabsf(cur[1][v] - q.h2));
         }
@@ -1135,11 +1161,35 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int64_t B, int64_t T, int64
   return g;
 }
 
-// tile configurations (V channels per lane, L steps per lane, NW waves per workgroup); the same
-// values instantiate the kernels and size the workspaces
-template <int CELL> struct NewtonCfg { static constexpr int V = CELL == CELL_LSTM ? 1 : 2, L = 8, NW = 16; };
-template <int S> struct ScanCfg { static constexpr int V = 1, L = S == 1 ? 16 : 8, NW = 16; };
-template <int CELL> struct VjpCfg { static constexpr int V = 1, L = CELL == CELL_LSTM ? 4 : 8, NW = 16; };
+// tile configurations (V channels per lane, L steps per lane, NW waves per workgroup, and the
+// minimum waves per SIMD the register allocation must leave room for); the same values instantiate
+// the kernels and size the workspaces.  The PR_* macros exist for tuning builds.
+#ifndef PR_GRU_CFG
+#define PR_GRU_CFG 2, 8, 16, 4
+#endif
+#ifndef PR_LSTM_CFG
+#define PR_LSTM_CFG 1, 8, 16, 4
+#endif
+#ifndef PR_SCAN1_CFG
+#define PR_SCAN1_CFG 1, 16, 16, 4
+#endif
+#ifndef PR_SCAN2_CFG
+#define PR_SCAN2_CFG 1, 8, 16, 4
+#endif
+#ifndef PR_VJP_GRU_CFG
+#define PR_VJP_GRU_CFG 1, 8, 16, 4
+#endif
+#ifndef PR_VJP_LSTM_CFG
+#define PR_VJP_LSTM_CFG 1, 4, 16, 4
+#endif
+template <int V_, int L_, int NW_, int MINW_>
+struct TileCfg { static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_; };
+template <int CELL> struct NewtonCfg : TileCfg<PR_GRU_CFG> {};
+template <> struct NewtonCfg<CELL_LSTM> : TileCfg<PR_LSTM_CFG> {};
+template <int S> struct ScanCfg : TileCfg<PR_SCAN1_CFG> {};
+template <> struct ScanCfg<2> : TileCfg<PR_SCAN2_CFG> {};
+template <int CELL> struct VjpCfg : TileCfg<PR_VJP_GRU_CFG> {};
+template <> struct VjpCfg<CELL_LSTM> : TileCfg<PR_VJP_LSTM_CFG> {};
 
 Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int ticket_slot) {
   Common c;
@@ -1203,57 +1253,62 @@ int64_t problem_N(const pararnn_problem* pb) { return pb->B * pb->T * pb->D; }
 template <int CELL, int DT>
 struct NewtonKernel {
   using C = NewtonCfg<CELL>;
-  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW>;
+  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW, C::MINW>;
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
   }
   static size_t ws(const pararnn_problem* pb) { return kHeader + align256(geo(pb).lb_bytes()); }
-  static pararnn_status run(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out, void* ws,
-                            hipStream_t st) {
+  static pararnn_status prepare(const pararnn_problem* pb, void* ws, hipStream_t st) {
     const Geo g = geo(pb);
     if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
-    pararnn_status rc = launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
-    if (rc) return rc;
+    return launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
+  }
+  static pararnn_status iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
+                                void* ws, hipStream_t st) {
+    const Geo g = geo(pb);
+    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
     uint32_t* res = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kResOffset);
-    for (int k = 0; k < op->max_iters; ++k) {
-      typename Op::Args a;
-      a.c = make_common(ws, g, pb->B, pb->T, pb->D, k);
-      a.c.tag = next_tag();
-      for (int i = 0; i < 4; ++i) a.pre[i] = pb->pre[i];
-      a.w = pb->w;
-      a.bias = pb->bias;
-      a.s0 = pb->s0;
-      a.h_in = (k == 0) ? op->init_guess : s_out;
-      a.h_out = s_out;
-      a.res_slot = res + k;
-      a.res_hist = res;
-      a.k = k;
-      a.tol = op->tol;
-      a.B = pb->B;
-      rc = launch_tile<Op>(a, g, st);
-      if (rc) return rc;
-    }
-    if (op->final_residual) {
-      constexpr int RV = 2, RL = 16;
-      const int64_t C = pb->B * pb->D;
-      const int64_t threads = ((C + RV - 1) / RV) * ((pb->T + RL - 1) / RL);
-      const int64_t blocks = (threads + 255) / 256;
-      hipLaunchKernelGGL((k_residual<CELL, DT, RV, RL>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                         pb->pre[0], pb->pre[1], pb->pre[2], pb->pre[3], pb->w, pb->bias, pb->s0, s_out, pb->B,
-                         pb->T, pb->D, res + PARARNN_MAX_ITERS);
-      if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
-    }
-    return PARARNN_OK;
+    typename Op::Args a;
+    a.c = make_common(ws, g, pb->B, pb->T, pb->D, k);
+    a.c.tag = next_tag();
+    for (int i = 0; i < 4; ++i) a.pre[i] = pb->pre[i];
+    a.w = pb->w;
+    a.bias = pb->bias;
+    a.s0 = pb->s0;
+    a.h_in = (k == 0) ? op->init_guess : s_out;
+    a.h_out = s_out;
+    a.res_slot = res + k;
+    a.res_hist = res;
+    a.k = k;
+    a.tol = op->tol;
+    a.B = pb->B;
+    return launch_tile<Op>(a, g, st);
+  }
+  static pararnn_status final_residual(const pararnn_problem* pb, const float* s_out, void* ws, hipStream_t st) {
+    uint32_t* res = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kResOffset);
+    constexpr int RV = 2, RL = 16;
+    const int64_t C = pb->B * pb->D;
+    const int64_t threads = ((C + RV - 1) / RV) * ((pb->T + RL - 1) / RL);
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL((k_residual<CELL, DT, RV, RL>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       pb->pre[0], pb->pre[1], pb->pre[2], pb->pre[3], pb->w, pb->bias, pb->s0, s_out, pb->B,
+                       pb->T, pb->D, res + PARARNN_MAX_ITERS);
+    return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
   }
 };
 
 struct NewtonEntry {
   size_t (*ws)(const pararnn_problem*);
-  pararnn_status (*run)(const pararnn_problem*, const pararnn_newton_opts*, float*, void*, hipStream_t);
+  pararnn_status (*prepare)(const pararnn_problem*, void*, hipStream_t);
+  pararnn_status (*iterate)(const pararnn_problem*, const pararnn_newton_opts*, int, float*, void*, hipStream_t);
+  pararnn_status (*final_residual)(const pararnn_problem*, const float*, void*, hipStream_t);
 };
 
 template <int CELL, int DT>
-NewtonEntry newton_entry() { return {NewtonKernel<CELL, DT>::ws, NewtonKernel<CELL, DT>::run}; }
+NewtonEntry newton_entry() {
+  using K = NewtonKernel<CELL, DT>;
+  return {K::ws, K::prepare, K::iterate, K::final_residual};
+}
 
 NewtonEntry pick_newton(int cell, int dt) {
   if (cell == CELL_GRU) return dt == DT_BF16 ? newton_entry<CELL_GRU, DT_BF16>() : newton_entry<CELL_GRU, DT_F32>();
@@ -1265,7 +1320,7 @@ NewtonEntry pick_newton(int cell, int dt) {
 template <int S, int DT, bool REV>
 struct ScanKernel {
   using C = ScanCfg<S>;
-  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW>;
+  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW, C::MINW>;
   static Geo geo(int64_t B, int64_t T, int64_t D) { return make_geo(S, Op::NSLOT, C::V, C::L, C::NW, B, T, D); }
   static size_t ws(int64_t B, int64_t T, int64_t D) { return kHeader + align256(geo(B, T, D).lb_bytes()); }
   static pararnn_status run(int64_t B, int64_t T, int64_t D, const void* a_, const void* b_, const float* s0,
@@ -1307,7 +1362,7 @@ ScanEntry pick_scan(int S, int dt, int rev) {
 template <int CELL, int DT>
 struct VjpKernel {
   using C = VjpCfg<CELL>;
-  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW>;
+  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW>;
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
   }
@@ -1345,7 +1400,8 @@ struct VjpKernel {
     if constexpr (Op::NPAR > 0) {
       if (d_w || d_bias) {
         const int64_t n = Op::NPAR * pb->D;
-        hipLaunchKernelGGL(k_param_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_param_reduce, dim3(static_cast<unsigned>((n + kRedCols - 1) / kRedCols)),
+                           dim3(kRedCols * kRedRows), 0, st,
                            a.partial, g.n_chunks, Op::NPAR, pb->B, pb->D, d_w, d_bias, Op::G);
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
       }
@@ -1396,24 +1452,51 @@ size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_n
   return pick_newton(pb->cell, pb->pre_dtype).ws(pb);
 }
 
-pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out, void* ws,
-                                    size_t ws_bytes, void* stream, pararnn_report* report) {
+namespace {
+// common validation of the Newton entry points; `need_out` checks s_out as well
+pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
+                            bool need_out, void* ws, size_t ws_bytes) {
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
   if (!op || op->max_iters < 1 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (problem_N(pb) == 0) return PARARNN_OK;
+  if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
+  if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb->cell, pb->pre_dtype).ws(pb)) return PARARNN_ERR_WORKSPACE;
+  return PARARNN_OK;
+}
+}  // namespace
+
+pararnn_status pararnn_newton_prepare(const pararnn_problem* pb, const pararnn_newton_opts* op, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  pararnn_status rc = newton_check(pb, op, nullptr, false, ws, ws_bytes);
+  if (rc || problem_N(pb) == 0) return rc;
+  return pick_newton(pb->cell, pb->pre_dtype).prepare(pb, ws, static_cast<hipStream_t>(stream));
+}
+
+pararnn_status pararnn_newton_iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  pararnn_status rc = newton_check(pb, op, s_out, true, ws, ws_bytes);
+  if (rc || problem_N(pb) == 0) return rc;
+  if (k < 0 || k >= op->max_iters) return PARARNN_ERR_INVALID_ARG;
+  return pick_newton(pb->cell, pb->pre_dtype).iterate(pb, op, k, s_out, ws, static_cast<hipStream_t>(stream));
+}
+
+pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
+                                     void* ws, size_t ws_bytes, void* stream, pararnn_report* report) {
+  pararnn_status rc = newton_check(pb, op, s_out, op && op->final_residual, ws, ws_bytes);
+  if (rc) return rc;
   if (report) std::memset(report, 0, sizeof(*report));
-  const int64_t N = problem_N(pb);
-  if (N == 0) {
+  if (problem_N(pb) == 0) {
     if (report) report->converged = op->tol > 0.0f ? 1 : 0;
     return PARARNN_OK;
   }
-  if (!s_out || !aligned(s_out, 8)) return PARARNN_ERR_INVALID_ARG;
-  if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
-  const NewtonEntry ne = pick_newton(pb->cell, pb->pre_dtype);
-  if (!ws || !aligned(ws, 256) || ws_bytes < ne.ws(pb)) return PARARNN_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = ne.run(pb, op, s_out, ws, st);
-  if (rc || !report) return rc;
+  if (op->final_residual) {
+    rc = pick_newton(pb->cell, pb->pre_dtype).final_residual(pb, s_out, ws, st);
+    if (rc) return rc;
+  }
+  if (!report) return PARARNN_OK;
   uint32_t res[PARARNN_MAX_ITERS + 1];
   if (hipMemcpyAsync(res, static_cast<char*>(ws) + kResOffset, sizeof(res), hipMemcpyDeviceToHost, st) != hipSuccess)
     return PARARNN_ERR_HIP;
@@ -1429,6 +1512,7 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
       if (r < op->tol) { iters = k + 1; conv = 1; break; }
     }
   }
+  for (int k = iters; k < op->max_iters; ++k) report->residual[k] = 0.0f;
   report->iters = iters;
   report->converged = conv;
   report->n_residual = iters;
@@ -1439,6 +1523,20 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
     report->n_residual = iters + 1;
   }
   return out;
+}
+
+pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out, void* ws,
+                                    size_t ws_bytes, void* stream, pararnn_report* report) {
+  pararnn_status rc = newton_check(pb, op, s_out, true, ws, ws_bytes);
+  if (rc) return rc;
+  if (problem_N(pb) == 0) return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
+  const NewtonEntry ne = pick_newton(pb->cell, pb->pre_dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = ne.prepare(pb, ws, st);
+  for (int k = 0; k < op->max_iters && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+  if (rc) return rc;
+  if (!report && !op->final_residual) return PARARNN_OK;
+  return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
 }
 
 size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True, text=True).stdout
@@ -98,6 +98,9 @@ def test_validation_codes_without_launching(lib):
     assert solve(_problem(), w=ctypes.c_void_p(4096 + 8)) == -3   # not 256-byte aligned
     assert solve(_problem(), n=16) == -3
     assert solve(_problem(T=0)) == 0                        # empty problem: no-op
+    it = lambda p, k: lib.pararnn_newton_iterate(ctypes.byref(p), ctypes.byref(opts), k, out, ws, 1 << 40, None)  # noqa
+    assert it(_problem(), -1) == -1 and it(_problem(), 3) == -1   # k outside [0, max_iters)
+    assert lib.pararnn_newton_prepare(ctypes.byref(_problem()), ctypes.byref(opts), ws, 16, None) == -3
     scan = lambda S, dt, a=4096, n=1 << 40: lib.pararnn_linear_scan(  # noqa: E731
         S, 8, 100, 64, dt, ctypes.c_void_p(a), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 0,
         ctypes.c_void_p(1 << 20), n, None)
