@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-channels", type=int, default=0, help="channels in the CPU-baseline sample (0: auto)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the hot path, time a plain device-to-device copy of this many MiB "
+                         "(same-box bandwidth context, and the known-size kernel that calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported (the hot path shards "
@@ -81,6 +84,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_mib > 0:
+        copy_bench(torch, dev, args)
+        return
     wl = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(wl)
     if wl.dtype == "bf16":
@@ -174,6 +180,25 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, iters, args.cpu_channels)
     print(json.dumps(line), flush=True)
+
+
+def copy_bench(torch, dev, args):
+    n = args.copy_mib * (1 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * n * 4
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
+                      "gbs": nbytes / (ms * 1e-3) / 1e9, "steps": args.steps}), flush=True)
 
 
 def cpu_baseline(wl, inp, iters, n_channels):

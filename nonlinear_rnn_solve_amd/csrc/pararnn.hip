@@ -190,11 +190,16 @@ struct Common {
   int64_t T, D, C, N;   // time steps, channels per row, B*D channels, B*T*D elements
 };
 
+// A tile is TW channels x CT steps.  A wave's 64 lanes form TS time slices of 64/TS lanes; lane
+// (slice s, position j) owns channels [j*V, j*V+V) of the tile and L consecutive steps; the NW*TS
+// segments of L steps are stacked in time: wave w, slice s -> segment w*TS + s.
 struct Tile {
   int64_t p, chunk, t_lo, ch0, b, d0;
-  int chain, wave, lane;
-  int nvalid;   // steps of this lane inside [0, T); the same for every lane of the wave
-  bool active;
+  int chain, wave, lane, slice, qlane;
+  int nvalid;        // steps of this lane inside [0, T); the same for every lane of a slice
+  bool active;       // the lane's channels exist
+  bool first_seg;    // this lane holds the tile's first segment in time (wave 0, slice 0)
+  bool last_seg;     // ... the tile's last segment in time
 };
 
 // row of step t clamped into [0, T): loads use clamped addresses and masked steps are replaced by
@@ -215,7 +220,7 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int q = tl.lane * V + v;
+    const int q = tl.qlane * V + v;
     Aff<S> acc = aff_id<S>();
     int64_t m = tl.p - 1;
     bool done = false;
@@ -277,15 +282,27 @@ DEV float wave_nanmax(float m) {
 // ------------------------------------------------------------------------------------------------
 // the generic tile kernel
 // ------------------------------------------------------------------------------------------------
+template <int S>
+DEV Aff<S> shfl_aff(const Aff<S>& m, int src) {
+  Aff<S> r;
+#pragma unroll
+  for (int k = 0; k < S * S; ++k) r.A[k] = __shfl(m.A[k], src, WAVE);
+#pragma unroll
+  for (int k = 0; k < S; ++k) r.b[k] = __shfl(m.b[k], src, WAVE);
+  return r;
+}
+
 template <class Op>
 __global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(Op::MINW)))
 void k_tile(const typename Op::Args a) {
-  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TW = WAVE * V, NA = S * S + S;
+  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS, NA = S * S + S;
+  constexpr int LPR = WAVE / TS, TW = LPR * V;
   constexpr int NSLOT = Op::NSLOT;
   constexpr bool REV = Op::REVERSE;
+  static_assert(TS == 1 || TS == 2 || TS == 4, "time slices per wave");
   __shared__ uint32_t sh_ticket;
-  __shared__ float sh_agg[NA][NW][TW];
-  __shared__ float sh_carry[S][TW];
+  __shared__ float sh_agg[NA][NW][TW];     // aggregate of each wave's TS*L steps
+  __shared__ float sh_carry[S][NW][TW];    // state entering each wave's steps (in scan order)
   __shared__ float sh_red[NW];
 
   if (Op::skip(a)) return;  // uniform: decided from values written by earlier launches
@@ -296,14 +313,18 @@ void k_tile(const typename Op::Args a) {
   Tile tl;
   tl.lane = threadIdx.x % WAVE;
   tl.wave = threadIdx.x / WAVE;
+  tl.slice = tl.lane / LPR;
+  tl.qlane = tl.lane % LPR;
   tl.p = sh_ticket / static_cast<uint32_t>(c.n_chains);
   tl.chain = static_cast<int>(sh_ticket % static_cast<uint32_t>(c.n_chains));
   tl.chunk = REV ? c.n_chunks - 1 - tl.p : tl.p;
-  tl.t_lo = tl.chunk * static_cast<int64_t>(NW * L) + tl.wave * L;
-  tl.ch0 = static_cast<int64_t>(tl.chain) * TW + tl.lane * V;
+  tl.t_lo = tl.chunk * static_cast<int64_t>(NW * TS * L) + (tl.wave * TS + tl.slice) * L;
+  tl.ch0 = static_cast<int64_t>(tl.chain) * TW + tl.qlane * V;
   tl.active = tl.ch0 < c.C;
   tl.b = tl.active ? tl.ch0 / c.D : 0;
   tl.d0 = tl.active ? tl.ch0 - tl.b * c.D : 0;
+  tl.first_seg = tl.wave == 0 && tl.slice == 0;
+  tl.last_seg = tl.wave == NW - 1 && tl.slice == TS - 1;
   {
     const int64_t left = c.T - tl.t_lo;
     tl.nvalid = static_cast<int>(left < 0 ? 0 : (left > L ? L : left));
@@ -312,15 +333,34 @@ void k_tile(const typename Op::Args a) {
   typename Op::Lane ln;
   float rmax = Op::produce(a, tl, ln);
 
-  // per-lane aggregate over its L steps, in scan order
-  const int q0 = tl.lane * V;
+  // per-lane aggregate over its L steps, in scan order; then across the wave's TS slices
+  const int q0 = tl.qlane * V;
+  const int sp = REV ? TS - 1 - tl.slice : tl.slice;   // the slice's position in scan order
+  Aff<S> excl[V];                                      // slices of this wave before mine, composed
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     Aff<S> g = aff_id<S>();
 #pragma unroll
     for (int s = 0; s < L; ++s) g = compose(ln.e[v][REV ? L - 1 - s : s], g);
+    excl[v] = aff_id<S>();
+    if constexpr (TS > 1) {
+      // inclusive scan over slices (Hillis-Steele on lanes LPR apart), then shift by one slice
+      Aff<S> inc = g;
 #pragma unroll
-    for (int k = 0; k < NA; ++k) sh_agg[k][tl.wave][q0 + v] = aff_get(g, k);
+      for (int d = 1; d < TS; d <<= 1) {
+        const int src = tl.lane + (REV ? d : -d) * LPR;
+        const Aff<S> o = shfl_aff(inc, (src + WAVE) % WAVE);
+        if (sp >= d) inc = compose(inc, o);
+      }
+      const int src = tl.lane + (REV ? 1 : -1) * LPR;
+      const Aff<S> prev = shfl_aff(inc, (src + WAVE) % WAVE);
+      if (sp > 0) excl[v] = prev;
+      g = inc;
+    }
+    if (sp == TS - 1) {
+#pragma unroll
+      for (int k = 0; k < NA; ++k) sh_agg[k][tl.wave][q0 + v] = aff_get(g, k);
+    }
   }
   if constexpr (Op::RESID) {
     rmax = wave_nanmax(rmax);
@@ -336,7 +376,9 @@ void k_tile(const typename Op::Args a) {
     }
   }
 
-  if (tl.wave == 0) {
+  if (tl.wave == 0 && tl.slice == 0) {
+    // one lane per channel group: the tile's aggregate, the look-back, then every wave's entering
+    // state (so that each wave reads one value instead of re-composing the waves before it)
     float carry[V][S];
     Aff<S> tagg[V];
 #pragma unroll
@@ -380,27 +422,34 @@ void k_tile(const typename Op::Args a) {
       }
     }
 #pragma unroll
-    for (int v = 0; v < V; ++v)
+    for (int v = 0; v < V; ++v) {
+      float x[S];
 #pragma unroll
-      for (int k = 0; k < S; ++k) sh_carry[k][q0 + v] = carry[v][k];
+      for (int k = 0; k < S; ++k) x[k] = carry[v][k];
+#pragma unroll
+      for (int s = 0; s < NW; ++s) {
+        const int w = REV ? NW - 1 - s : s;
+#pragma unroll
+        for (int k = 0; k < S; ++k) sh_carry[k][w][q0 + v] = x[k];
+        if (s + 1 < NW) {
+          Aff<S> e;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) aff_set(e, k, sh_agg[k][w][q0 + v]);
+          apply(e, x);
+        }
+      }
+    }
   }
   __syncthreads();
 
-  // state entering this wave's steps: the tile carry advanced through the waves before it
+  // state entering this lane's steps: the wave's entering state advanced through earlier slices
   float x[V][S];
-  const int my_pos = REV ? NW - 1 - tl.wave : tl.wave;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     float xv[S];
 #pragma unroll
-    for (int k = 0; k < S; ++k) xv[k] = sh_carry[k][q0 + v];
-    for (int s = 0; s < my_pos; ++s) {
-      const int w = REV ? NW - 1 - s : s;
-      Aff<S> e;
-#pragma unroll
-      for (int k = 0; k < NA; ++k) aff_set(e, k, sh_agg[k][w][q0 + v]);
-      apply(e, xv);
-    }
+    for (int k = 0; k < S; ++k) xv[k] = sh_carry[k][tl.wave][q0 + v];
+    if constexpr (TS > 1) apply(excl[v], xv);
 #pragma unroll
     for (int k = 0; k < S; ++k) x[v][k] = xv[k];
   }
@@ -530,9 +579,9 @@ DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&
 // ------------------------------------------------------------------------------------------------
 // Op 1: linear recurrence (pararnn_linear_scan)
 // ------------------------------------------------------------------------------------------------
-template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_>
+template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_, int TS_>
 struct LinearOp {
-  static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_;
+  static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = REV, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
@@ -612,10 +661,10 @@ struct LinearOp {
 //   r_t = h^k_t - f_t (the same iterate, written without forming delta).  The max |r_t| is
 //   reduced for the tolerance test.  LINEAR: the element is (a_t, b_t) itself.
 // ------------------------------------------------------------------------------------------------
-template <int CELL, int DT, int V_, int L_, int NW_, int MINW_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_>
 struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
-  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_;
+  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
@@ -655,8 +704,8 @@ struct NewtonOp {
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
     const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
     const Common& c = a.c;
-    constexpr int TW = WAVE * V;
-    const int q0 = tl.lane * V;
+    constexpr int TW = (WAVE / TS) * V;
+    const int q0 = tl.qlane * V;
     const bool have_h = a.h_in != nullptr;
     // loads first, all of them: the current iterate at steps t_lo-1 .. t_lo+L-1 (h[.][0] is the
     // step before the lane's first) and the gate inputs of the lane's L steps
@@ -669,7 +718,7 @@ struct NewtonOp {
 #pragma unroll
         for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.h_in, k * N + (row + t) * D + tl.d0, h[k][i + 1]);
       }
-      if (tl.wave != 0) {
+      if (!tl.first_seg) {
         // h^k_{t_lo-1} lies in this tile's chunk (written only after the tile's look-back)
         const int64_t idx = (row + clamp_t(tl.t_lo - 1, T)) * D + tl.d0;
 #pragma unroll
@@ -702,14 +751,14 @@ struct NewtonOp {
     if (have_h && tl.active) {
       // publish this tile's last state (the h^k the next tile's first step needs), then take the
       // previous tile's: the trajectory is updated in place, so it cannot be re-read from memory
-      if (tl.wave == NW - 1 && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
+      if (tl.last_seg && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
           for (int k = 0; k < S; ++k)
             st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, HALO + k, q0 + v), c.tag, h[k][L][v]);
       }
-      if (tl.wave == 0 && tl.t_lo != 0) {
+      if (tl.first_seg && tl.t_lo != 0) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -795,10 +844,10 @@ template <> struct VjpStash<CELL_LINEAR> { float hp; };
 template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
 template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
 
-template <int CELL, int DT, int V_, int L_, int NW_, int MINW_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_>
 struct VjpOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
-  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_;
+  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = true, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
@@ -924,9 +973,9 @@ struct VjpOp {
     }
   }
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
-    constexpr int TW = WAVE * V;
+    constexpr int TW = (WAVE / TS) * V, NSEG = NW * TS;
     constexpr int NP = NPAR > 0 ? NPAR : 1;
-    __shared__ float sh_par[NP][NW][TW];
+    __shared__ float sh_par[NP][NSEG][TW];
     const int64_t D = a.c.D, T = a.c.T, N = a.c.N;
     float par[V][NP];
 #pragma unroll
@@ -994,11 +1043,11 @@ struct VjpOp {
       }
     }
     if constexpr (NPAR > 0) {
-      const int q0 = tl.lane * V;
+      const int q0 = tl.qlane * V, seg = tl.wave * TS + tl.slice;
 #pragma unroll
       for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int j = 0; j < NPAR; ++j) sh_par[j][tl.wave][q0 + v] = par[v][j];
+        for (int j = 0; j < NPAR; ++j) sh_par[j][seg][q0 + v] = par[v][j];
       __syncthreads();
       // fixed-order sum over the waves of the tile
       for (int idx = threadIdx.x; idx < NPAR * TW; idx += NW * WAVE) {
@@ -1006,7 +1055,7 @@ struct VjpOp {
         const int64_t ch = static_cast<int64_t>(tl.chain) * TW + q;
         if (ch >= a.c.C) continue;
         float sum = 0.0f;
-        for (int w = 0; w < NW; ++w) sum += sh_par[j][w][q];
+        for (int w = 0; w < NSEG; ++w) sum += sh_par[j][w][q];
         a.partial[(tl.chunk * NPAR + j) * a.c.C + ch] = sum;
       }
     }
@@ -1150,11 +1199,11 @@ struct Geo {
   }
 };
 
-Geo make_geo(int S, int nslot, int V, int L, int NW, int64_t B, int64_t T, int64_t D) {
+Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t T, int64_t D) {
   Geo g;
   g.V = V; g.L = L; g.NW = NW; g.S = S; g.nslot = nslot;
-  g.TW = WAVE * V;
-  g.CT = static_cast<int64_t>(NW) * L;
+  g.TW = (WAVE / TS) * V;
+  g.CT = static_cast<int64_t>(NW) * TS * L;
   const int64_t C = B * D;
   g.n_chains = (C + g.TW - 1) / g.TW;
   g.n_chunks = (T + g.CT - 1) / g.CT;
@@ -1165,25 +1214,25 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int64_t B, int64_t T, int64
 // minimum waves per SIMD the register allocation must leave room for); the same values instantiate
 // the kernels and size the workspaces.  The PR_* macros exist for tuning builds.
 #ifndef PR_GRU_CFG
-#define PR_GRU_CFG 2, 8, 16, 4
+#define PR_GRU_CFG 2, 8, 8, 4, 2
 #endif
 #ifndef PR_LSTM_CFG
-#define PR_LSTM_CFG 1, 8, 16, 4
+#define PR_LSTM_CFG 1, 8, 8, 4, 2
 #endif
 #ifndef PR_SCAN1_CFG
-#define PR_SCAN1_CFG 1, 16, 16, 4
+#define PR_SCAN1_CFG 1, 16, 16, 4, 1
 #endif
 #ifndef PR_SCAN2_CFG
-#define PR_SCAN2_CFG 1, 8, 16, 4
+#define PR_SCAN2_CFG 1, 8, 16, 4, 1
 #endif
 #ifndef PR_VJP_GRU_CFG
-#define PR_VJP_GRU_CFG 1, 8, 16, 4
+#define PR_VJP_GRU_CFG 1, 8, 16, 4, 1
 #endif
 #ifndef PR_VJP_LSTM_CFG
-#define PR_VJP_LSTM_CFG 1, 4, 16, 4
+#define PR_VJP_LSTM_CFG 1, 4, 16, 4, 1
 #endif
-template <int V_, int L_, int NW_, int MINW_>
-struct TileCfg { static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_; };
+template <int V_, int L_, int NW_, int MINW_, int TS_>
+struct TileCfg { static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_; };
 template <int CELL> struct NewtonCfg : TileCfg<PR_GRU_CFG> {};
 template <> struct NewtonCfg<CELL_LSTM> : TileCfg<PR_LSTM_CFG> {};
 template <int S> struct ScanCfg : TileCfg<PR_SCAN1_CFG> {};
@@ -1253,9 +1302,9 @@ int64_t problem_N(const pararnn_problem* pb) { return pb->B * pb->T * pb->D; }
 template <int CELL, int DT>
 struct NewtonKernel {
   using C = NewtonCfg<CELL>;
-  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW, C::MINW>;
+  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS>;
   static Geo geo(const pararnn_problem* pb) {
-    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
+    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
   static size_t ws(const pararnn_problem* pb) { return kHeader + align256(geo(pb).lb_bytes()); }
   static pararnn_status prepare(const pararnn_problem* pb, void* ws, hipStream_t st) {
@@ -1320,8 +1369,8 @@ NewtonEntry pick_newton(int cell, int dt) {
 template <int S, int DT, bool REV>
 struct ScanKernel {
   using C = ScanCfg<S>;
-  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW, C::MINW>;
-  static Geo geo(int64_t B, int64_t T, int64_t D) { return make_geo(S, Op::NSLOT, C::V, C::L, C::NW, B, T, D); }
+  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW, C::MINW, C::TS>;
+  static Geo geo(int64_t B, int64_t T, int64_t D) { return make_geo(S, Op::NSLOT, C::V, C::L, C::NW, C::TS, B, T, D); }
   static size_t ws(int64_t B, int64_t T, int64_t D) { return kHeader + align256(geo(B, T, D).lb_bytes()); }
   static pararnn_status run(int64_t B, int64_t T, int64_t D, const void* a_, const void* b_, const float* s0,
                             float* out, void* ws, hipStream_t st) {
@@ -1362,9 +1411,9 @@ ScanEntry pick_scan(int S, int dt, int rev) {
 template <int CELL, int DT>
 struct VjpKernel {
   using C = VjpCfg<CELL>;
-  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW>;
+  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS>;
   static Geo geo(const pararnn_problem* pb) {
-    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, pb->B, pb->T, pb->D);
+    return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
   static size_t part_bytes(const Geo& g, const pararnn_problem* pb) {
     return static_cast<size_t>(g.n_chunks) * Op::NPAR * pb->B * pb->D * sizeof(float);
