@@ -50,6 +50,28 @@ def vjp_bytes(cell: str, dtype: str) -> int:
     return G * esz + 4 * S + 4 + 4 * G
 
 
+def source_hash() -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "nonlinear_rnn_solve_amd", "csrc", "pararnn.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same
+    counter reads for a copy of known size), or None when that summary was taken on other source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(key)
+    return None if k is None else float(k["bytes_per_launch"])
+
+
 def cpu_threads() -> int:
     n = os.cpu_count() or 1
     try:
@@ -163,6 +185,7 @@ def main():
     achieved = per_elem * N / (kern_ms * 1e-3) / 1e9
     value = N * iters / (ms_per_step * 1e-3)
     kernel_name = "k_tile<LinearOp>" if wl.cell == "linear" else "k_tile<NewtonOp> (iterations k>=1)"
+    traffic = measured_traffic(wl.name)
     line = {
         "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -170,8 +193,8 @@ def main():
         "config": {"workload": wl.name, "cell": wl.cell, "B": wl.B, "T": wl.T, "D": wl.D, "storage": wl.dtype,
                    "tol": wl.tol, "max_iters": wl.max_iters, "iters": iters, "vjp": wl.vjp},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel_name,
-                     "bytes_per_elem": per_elem, "kernel_ms": kern_ms},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel_name,
+                     "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms},
     }
     if vjp_events:
         vms = float(np.mean([a.elapsed_time(b2) for a, b2 in vjp_events]))
