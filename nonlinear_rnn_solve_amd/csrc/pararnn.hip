@@ -62,44 +62,74 @@ DEV float tanh_(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(2.0f * kLog2
 DEV float nanmax(float m, float x) { return (x > m || x != x) ? x : m; }
 
 // ------------------------------------------------------------------------------------------------
-// vector loads / stores of V consecutive channels
+// vector loads / stores of V consecutive channels.  Streaming data (read or written once per pass) uses
+// non-temporal accesses when PR_NT_LOAD / PR_NT_STORE are set.
 // ------------------------------------------------------------------------------------------------
+#ifndef PR_NT_LOAD
+#define PR_NT_LOAD 0
+#endif
+#ifndef PR_NT_STORE
+#define PR_NT_STORE 1
+#endif
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+DEV T ld_stream(const T* p) {
+  if constexpr (PR_NT_LOAD) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+DEV void st_stream(T* p, T v) {
+  if constexpr (PR_NT_STORE) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 template <int V, int DT>
 DEV void ldv(const void* base, int64_t idx, float (&o)[V]) {
   if constexpr (DT == DT_F32) {
     const float* p = static_cast<const float*>(base) + idx;
     if constexpr (V == 1) {
-      o[0] = p[0];
+      o[0] = ld_stream(p);
     } else if constexpr (V == 2) {
-      float2 t = *reinterpret_cast<const float2*>(p);
+      const f32x2 t = ld_stream(reinterpret_cast<const f32x2*>(p));
       o[0] = t.x; o[1] = t.y;
     } else {
-      float4 t = *reinterpret_cast<const float4*>(p);
+      const f32x4 t = ld_stream(reinterpret_cast<const f32x4*>(p));
       o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
     }
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
     if constexpr (V == 1) {
-      o[0] = __uint_as_float(static_cast<uint32_t>(p[0]) << 16);
+      o[0] = __uint_as_float(static_cast<uint32_t>(ld_stream(p)) << 16);
     } else if constexpr (V == 2) {
-      uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+      const uint32_t t = ld_stream(reinterpret_cast<const uint32_t*>(p));
       o[0] = __uint_as_float(t << 16); o[1] = __uint_as_float(t & 0xffff0000u);
     } else {
-      uint2 t = *reinterpret_cast<const uint2*>(p);
+      const u32x2 t = ld_stream(reinterpret_cast<const u32x2*>(p));
       o[0] = __uint_as_float(t.x << 16); o[1] = __uint_as_float(t.x & 0xffff0000u);
       o[2] = __uint_as_float(t.y << 16); o[3] = __uint_as_float(t.y & 0xffff0000u);
     }
   }
 }
 
+// small per-channel parameter vectors (re-read by every tile): plain cached loads
+template <int V>
+DEV void ldv_param(const float* base, int64_t idx, float (&o)[V]) {
+  const float* p = base + idx;
+#pragma unroll
+  for (int v = 0; v < V; ++v) o[v] = p[v];
+}
+
 template <int V>
 DEV void stv(float* p, const float (&x)[V]) {
   if constexpr (V == 1) {
-    p[0] = x[0];
+    st_stream(p, x[0]);
   } else if constexpr (V == 2) {
-    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    st_stream(reinterpret_cast<f32x2*>(p), f32x2{x[0], x[1]});
   } else {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    st_stream(reinterpret_cast<f32x4*>(p), f32x4{x[0], x[1], x[2], x[3]});
   }
 }
 
@@ -480,8 +510,8 @@ template <int CELL, int G, int V>
 DEV void load_params(const float* w, const float* bias, int64_t D, int64_t d0, Params<G, V>& pm) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    ldv<V, DT_F32>(w, g * D + d0, pm.w[g]);
-    ldv<V, DT_F32>(bias, g * D + d0, pm.bias[g]);
+    ldv_param<V>(w, g * D + d0, pm.w[g]);
+    ldv_param<V>(bias, g * D + d0, pm.bias[g]);
     const float sc = gate_scale<CELL>(g);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
