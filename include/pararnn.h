@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PARARNN_ABI_VERSION 1
+#define PARARNN_ABI_VERSION 2
 /* upper bound of Newton iterations per call (report.residual holds one more) */
 #define PARARNN_MAX_ITERS 64
 
@@ -79,15 +79,22 @@ typedef struct {
   const float* s0;       /* [S][B][D] initial state h_{-1}; NULL = zeros                        */
 } pararnn_problem;
 
+/* First Newton iterate when no init_guess is given.  WARM is the GRU / LSTM warm start of the
+ * pararnn-torch README ("Method"): every step's state is the cell applied to a zero previous state,
+ * H^0_t = f(0, x_t) (for every t, s0 included: the guess does not use s0).  It is computed inside
+ * iteration 0's kernel from the gate inputs it loads anyway (no extra pass, no extra buffer).      */
+typedef enum { PARARNN_INIT_ZERO = 0, PARARNN_INIT_WARM = 1 } pararnn_init_mode;
+
 typedef struct {
   int32_t max_iters;       /* Newton budget K, 1..PARARNN_MAX_ITERS                                 */
   float tol;               /* <= 0: run exactly max_iters iterations.
                               > 0: iteration k evaluates R_k = max|r(H^k)| over b, t, d and state
                               components; the first iteration with R_k < tol is the last one (its
                               update is applied).  A non-finite R_k stops the solve (DIVERGED).     */
-  const float* init_guess; /* [S][B][T][D] first iterate H^0, or NULL for H^0 = 0.  May equal s_out
-                              (resume from a previous solve's output).                              */
+  const float* init_guess; /* [S][B][T][D] first iterate H^0, or NULL (then init_mode decides).  May
+                              equal s_out (resume from a previous solve's output).                  */
   int32_t final_residual;  /* nonzero: one extra pass computes max|r| of the returned trajectory   */
+  int32_t init_mode;       /* pararnn_init_mode; ignored when init_guess is non-NULL                 */
 } pararnn_newton_opts;
 
 typedef struct {          /* (host) */

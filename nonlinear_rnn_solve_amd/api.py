@@ -23,6 +23,8 @@ CELLS = {"linear": 0, "gru": 1, "lstm": 2}
 GATES = {0: 2, 1: 3, 2: 4}
 STATE = {0: 1, 1: 1, 2: 2}
 MAX_ITERS = 64
+ABI_VERSION = 2
+INIT_ZERO, INIT_WARM = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
           -5: "Newton diverged"}
 
@@ -50,7 +52,7 @@ class _Problem(ctypes.Structure):
 
 class _Opts(ctypes.Structure):
     _fields_ = [("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("init_guess", ctypes.c_void_p),
-                ("final_residual", ctypes.c_int32)]
+                ("final_residual", ctypes.c_int32), ("init_mode", ctypes.c_int32)]
 
 
 class _Report(ctypes.Structure):
@@ -104,7 +106,7 @@ def load_library():
     lib.pararnn_vjp_workspace_bytes.argtypes = [vp]
     lib.pararnn_scan_vjp.restype = i32
     lib.pararnn_scan_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    if lib.pararnn_abi_version() != 1:
+    if lib.pararnn_abi_version() != ABI_VERSION:
         raise RuntimeError("libpararnn.so ABI mismatch")
     _lib = lib
     return lib
@@ -180,12 +182,13 @@ def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
 
 
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
-                 final_residual=False, report=True, on_iteration=None):
+                 final_residual=False, report=True, on_iteration=None, warm_start=False):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
     tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
     (evaluated at its input iterate) is below tol.  report=True waits for the stream.
+    warm_start: without init_guess, start from H^0_t = f(0, x_t) instead of zeros.
     on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
     launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
     entry points prepare / iterate / report, which launch exactly the same kernels.
@@ -202,7 +205,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
         raise ValueError("init_guess must be [S, B, T, D]")
     opts = _Opts(int(max_iters), float(tol), init_guess.data_ptr() if init_guess is not None else None,
-                 1 if final_residual else 0)
+                 1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO)
     nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
     ws = _workspace(nbytes, dev, "newton")
     rep = _Report() if report else None

@@ -705,8 +705,9 @@ struct NewtonOp {
     const float* w;
     const float* bias;
     const float* s0;
-    const float* h_in;        // H^k [S][B][T][D], or NULL for H^k = 0
+    const float* h_in;        // H^k [S][B][T][D], or NULL for H^k = 0 (or the warm start)
     float* h_out;             // H^{k+1}; may equal h_in
+    int32_t warm;             // h_in == NULL: H^0_t = f(0, x_t) computed here instead of 0
     uint32_t* res_slot;       // max |r| of this iteration (float bits, atomicMax)
     const uint32_t* res_hist; // max |r| of earlier iterations
     int32_t k;
@@ -729,6 +730,18 @@ struct NewtonOp {
   }
   static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
     return tl.nvalid == L ? produce_t<false>(a, tl, ln) : produce_t<true>(a, tl, ln);
+  }
+  // f(0, u) for channel slot v (pararnn-torch README, "Method": the GRU / LSTM warm start)
+  static DEV void warm_state(const Params<G, V>& pm, int v, const float (&u)[G][V], float (&o)[S]) {
+    if constexpr (CELL == CELL_LINEAR) {
+      o[0] = u[1][v];
+    } else if constexpr (CELL == CELL_GRU) {
+      o[0] = gru_eval(pm, v, u[0][v], u[1][v], u[2][v], 0.0f).f;
+    } else {
+      const LstmPart q = lstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], 0.0f, 0.0f);
+      o[0] = q.c2;
+      o[1] = q.h2;
+    }
   }
   template <bool MASKED>
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
@@ -770,6 +783,30 @@ struct NewtonOp {
     }
     Params<G, V> pm;
     if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(a.w, a.bias, D, tl.d0, pm);
+    if (!have_h && a.warm) {
+      // warm first iterate: every step's state is the cell applied to a zero previous state, so
+      // h^0_{t_lo-1} needs only that step's gate inputs (no halo exchange in this iteration)
+      float up[G][V];
+      const int64_t tp = clamp_t(tl.t_lo - 1, T);
+#pragma unroll
+      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], (row + tp) * D + tl.d0, up[g]);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float o[S];
+        warm_state(pm, v, up, o);
+#pragma unroll
+        for (int k = 0; k < S; ++k) h[k][0][v] = o[k];
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+          float ui[G][V];
+#pragma unroll
+          for (int g = 0; g < G; ++g) ui[g][v] = u[g][i][v];
+          warm_state(pm, v, ui, o);
+#pragma unroll
+          for (int k = 0; k < S; ++k) h[k][i + 1][v] = o[k];
+        }
+      }
+    }
     if (tl.t_lo == 0) {
       float x[V][S];
       load_s0<S, V>(a.s0, a.B, D, tl, x);
@@ -1356,6 +1393,7 @@ struct NewtonKernel {
     a.s0 = pb->s0;
     a.h_in = (k == 0) ? op->init_guess : s_out;
     a.h_out = s_out;
+    a.warm = op->init_mode == PARARNN_INIT_WARM;
     a.res_slot = res + k;
     a.res_hist = res;
     a.k = k;
@@ -1538,6 +1576,7 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
   if (!op || op->max_iters < 1 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (op->init_mode != PARARNN_INIT_ZERO && op->init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;

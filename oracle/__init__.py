@@ -63,10 +63,10 @@ def _load():
         lib.or_cell_step.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.or_unroll.argtypes = [vp, vp, i32]
         lib.or_residual.argtypes = [vp, vp, vp, i32]
-        lib.or_newton.argtypes = [vp, vp, i32, dbl, vp, vp, vp, vp, i32]
+        lib.or_newton.argtypes = [vp, vp, i32, i32, dbl, vp, vp, vp, vp, i32]
         lib.or_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, i32, vp, i32]
         lib.or_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        assert lib.or_abi_version() == 3
+        assert lib.or_abi_version() == 4
         _lib = lib
     return _lib
 
@@ -158,13 +158,15 @@ def residual(prob: Problem, H, nthreads=None) -> float:
     return float(m[0])
 
 
-def newton(prob: Problem, max_iters, tol=0.0, init_guess=None, nthreads=None):
-    """Newton with sequential linear solves. Returns (H fp64, residuals[iters], iters, converged, status)."""
+def newton(prob: Problem, max_iters, tol=0.0, init_guess=None, nthreads=None, warm=False):
+    """Newton with sequential linear solves. Returns (H fp64, residuals[iters], iters, converged, status).
+
+    warm=True starts from H^0_t = f(0, x_t) (ignored when init_guess is given)."""
     H = np.zeros(prob.traj_shape(), dtype=np.float64)
     res = np.zeros(max(1, max_iters))
     it, conv = ctypes.c_int(0), ctypes.c_int(0)
     ig = None if init_guess is None else np.ascontiguousarray(init_guess, dtype=np.float32).reshape(prob.traj_shape())
-    rc = _check(_load().or_newton(ctypes.byref(prob.struct), _ptr(ig), int(max_iters), float(tol), _ptr(H),
+    rc = _check(_load().or_newton(ctypes.byref(prob.struct), _ptr(ig), 1 if warm else 0, int(max_iters), float(tol), _ptr(H),
                                   _ptr(res), ctypes.byref(it), ctypes.byref(conv), nthreads or default_threads()),
                 "newton")
     return H, res[: it.value].copy(), it.value, bool(conv.value), rc

@@ -395,7 +395,24 @@ static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   c->worker_max[worker] = m;
 }
 
-int or_newton(const or_problem* p, const float* init_guess, int max_iters, double tol,
+/* warm start (pararnn-torch README, "Method": the GRU/LSTM first iterate is the cell applied to a
+   zero previous state): H^0_t = f(0, x_t) for every t */
+static void warm_start(const or_problem* p, double* H) {
+  int S = state_size(p->cell);
+  double u[4], w[4], bias[4], zero[2] = {0.0, 0.0}, sn[2];
+  for (int64_t b = 0; b < p->B; ++b)
+    for (int64_t d = 0; d < p->D; ++d) {
+      gather_params(p, d, w, bias);
+      for (int64_t t = 0; t < p->T; ++t) {
+        gather_u(p, b, t, d, u);
+        or_cell_step(p->cell, u, w, bias, zero, sn, NULL, NULL, NULL);
+        for (int k = 0; k < S; ++k) H[traj_index(p, k, b, t, d)] = sn[k];
+      }
+    }
+}
+
+/* init_mode: 0 = init_guess or zeros, 1 = warm start (ignored when init_guess is given) */
+int or_newton(const or_problem* p, const float* init_guess, int init_mode, int max_iters, double tol,
               double* H, double* resid, int* iters, int* converged, int nthreads) {
   int rc = check_problem(p);
   if (rc) return rc;
@@ -403,6 +420,7 @@ int or_newton(const or_problem* p, const float* init_guess, int max_iters, doubl
   int S = state_size(p->cell);
   int64_t n = (int64_t)S * p->B * p->T * p->D;
   for (int64_t i = 0; i < n; ++i) H[i] = init_guess ? (double)init_guess[i] : 0.0;
+  if (!init_guess && init_mode == 1) warm_start(p, H);
   if (nthreads < 1) nthreads = 1;
   double* wm = (double*)malloc(sizeof(double) * (size_t)nthreads);
   double* scratch = (double*)malloc(sizeof(double) * (size_t)nthreads *
@@ -607,4 +625,4 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
 }
 
 /* ABI version of this file's entry points, so the wrapper can check it */
-int or_abi_version(void) { return 3; }
+int or_abi_version(void) { return 4; }

@@ -39,15 +39,17 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
                    ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0), sizeof(pararnn_newton_opts),'
-                   ' offsetof(pararnn_newton_opts, final_residual), sizeof(pararnn_report),'
+                   ' offsetof(pararnn_newton_opts, final_residual), offsetof(pararnn_newton_opts, init_mode),'
+                   ' sizeof(pararnn_report),'
                    ' offsetof(pararnn_report, residual)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
-            ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, ctypes.sizeof(api._Report),
+            ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, api._Opts.init_mode.offset,
+            ctypes.sizeof(api._Report),
             api._Report.residual.offset]
     assert got == want
 
@@ -94,6 +96,7 @@ def test_validation_codes_without_launching(lib):
     assert solve(p) == -1
     assert solve(_problem(), o=api._Opts(0, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
+    assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
     assert solve(_problem(), w=ctypes.c_void_p(0)) == -3
     assert solve(_problem(), w=ctypes.c_void_p(4096 + 8)) == -3   # not 256-byte aligned
     assert solve(_problem(), n=16) == -3
@@ -116,7 +119,7 @@ def test_validation_codes_without_launching(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.pararnn_status_string(s).decode() != "unknown status"
-    assert lib.pararnn_abi_version() == 1
+    assert lib.pararnn_abi_version() == api.ABI_VERSION == 2
 
 
 def test_binding_refuses_cpu_tensors():

@@ -129,6 +129,57 @@ def test_config0_exact_shape():
 
 
 # ------------------------------------------------------------------------------------------------
+# Newton, warm start H^0_t = f(0, x_t)
+# ------------------------------------------------------------------------------------------------
+WARM_CASES = [
+    ("gru", "f32", (2, 1000, 200), 1),
+    ("gru", "bf16", (2, 1000, 200), 3),
+    ("lstm", "f32", (2, 1000, 100), 2),
+    ("lstm", "bf16", (1, 777, 64), 1),
+    ("linear", "f32", (1, 300, 8), 1),
+    ("gru", "f32", (1, 1, 2), 1),
+    ("gru", "f32", (3, 129, 6), 2),
+    ("lstm", "f32", (1, 129, 66), 3),
+]
+
+
+@pytest.mark.parametrize("cell,dtype,shape,K", WARM_CASES)
+def test_newton_warm_start(cell, dtype, shape, K):
+    B, T, D = shape
+    announce("newton warm", cell, dtype, shape, K)
+    inp = synth.make_inputs(cell, B, T, D, dtype=dtype, seed=1450 + T + D)
+    s0 = synth.random_state(inp.S, B, D, seed=12)
+    H, res, *_ = oracle.newton(oracle_problem(inp, s0), K, warm=True)
+    got, rep = api.newton_solve(cell, dev_pre(inp), dev(inp.w), dev(inp.bias), max_iters=K, s0=dev(s0),
+                                warm_start=True)
+    err = max_abs(got.cpu().numpy(), H)
+    print("  max abs err", err, "residuals gpu", rep.residuals, "oracle", list(res))
+    assert err <= 1e-5 if dtype == "f32" else err <= 1e-4
+    np.testing.assert_allclose(rep.residuals, res, rtol=1e-3, atol=1e-5)
+
+
+def test_warm_start_is_ignored_with_an_initial_guess():
+    inp = synth.make_inputs("gru", 1, 600, 16, seed=1460)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    guess, _ = api.newton_solve("gru", pre, w, b, max_iters=1)
+    a, _ = api.newton_solve("gru", pre, w, b, max_iters=2, init_guess=guess.clone(), warm_start=True)
+    z, _ = api.newton_solve("gru", pre, w, b, max_iters=2, init_guess=guess.clone())
+    assert torch.equal(a, z)
+
+
+def test_warm_start_needs_no_more_iterations():
+    inp = synth.make_inputs("lstm", 2, 3000, 64, seed=1461)
+    prob = oracle_problem(inp)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    _, rz = api.newton_solve("lstm", pre, w, b, max_iters=10, tol=1e-5)
+    got, rw = api.newton_solve("lstm", pre, w, b, max_iters=10, tol=1e-5, warm_start=True)
+    print("  zero", rz.iters, rz.residuals, "warm", rw.iters, rw.residuals)
+    assert rw.converged and rw.iters <= rz.iters
+    assert rw.residuals[0] < rz.residuals[0]
+    assert max_abs(got.cpu().numpy(), oracle.unroll(prob)) <= 1e-4
+
+
+# ------------------------------------------------------------------------------------------------
 # Newton, tolerance mode
 # ------------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("cell,dtype,shape", [("gru", "bf16", (1, 4096, 64)), ("gru", "f32", (2, 2000, 32)),

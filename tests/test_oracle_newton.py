@@ -21,7 +21,14 @@ import oracle
 from nonlinear_rnn_solve_amd import synth
 from test_oracle_cells import torch_gru_cell, torch_lstm_cell
 
-torch.set_default_dtype(torch.float64)
+
+@pytest.fixture(autouse=True)
+def _fp64_default():
+    # the torch reference cells here run in fp64; restore the default so other modules are unaffected
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def dense_F(inp, s0):
@@ -164,3 +171,30 @@ def test_residual_of_unroll_is_rounding_level():
     prob = oracle.Problem("lstm", inp.pre, inp.w, inp.bias)
     assert oracle.residual(prob, oracle.unroll(prob)) == 0.0
     assert oracle.residual(prob, np.zeros(prob.traj_shape())) > 0.1
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_warm_start_is_the_cell_applied_to_a_zero_state(cell):
+    # the warm first iterate is f(0, x_t) at every t; pinned by passing that trajectory, computed with the
+    # torch library cell, as an explicit initial guess
+    inp = synth.make_inputs(cell, 2, 40, 3, seed=1018)
+    prob = oracle.Problem(cell, inp.pre, inp.w, inp.bias)
+    pre = [torch.tensor(p.astype(np.float64)) for p in inp.pre_f32()]
+    w, bias = inp.w.astype(np.float64), inp.bias.astype(np.float64)
+    x = torch.cat(pre, 2).reshape(2 * 40, -1)
+    z = torch.zeros(2 * 40, 3)
+    if cell == "gru":
+        f0 = torch_gru_cell(w, bias)(x, z).reshape(1, 2, 40, 3)
+    else:
+        h2, c2 = torch_lstm_cell(w, bias)(x, (z, z))
+        f0 = torch.stack([c2, h2]).reshape(2, 2, 40, 3)
+    guess = f0.detach().numpy().astype(np.float32)
+    for K in (1, 3):
+        Hw = oracle.newton(prob, K, warm=True)[0]
+        Hg = oracle.newton(prob, K, init_guess=guess)[0]
+        # the guess was rounded to fp32 once; the iterates differ only by that rounding
+        np.testing.assert_allclose(Hw, Hg, atol=1e-6)
+    # and the warm start's first residual is smaller than the zero guess's
+    _, rw, *_ = oracle.newton(prob, 1, warm=True)
+    _, rz, *_ = oracle.newton(prob, 1)
+    assert rw[0] < rz[0]

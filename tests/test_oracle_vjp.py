@@ -14,7 +14,14 @@ import oracle
 from nonlinear_rnn_solve_amd import synth
 from test_oracle_cells import torch_gru_cell, torch_lstm_cell
 
-torch.set_default_dtype(torch.float64)
+
+@pytest.fixture(autouse=True)
+def _fp64_default():
+    # the torch reference cells here run in fp64; restore the default so other modules are unaffected
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def autograd_reference(inp, s0, g):
