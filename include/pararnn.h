@@ -86,7 +86,8 @@ typedef struct {
 typedef enum { PARARNN_INIT_ZERO = 0, PARARNN_INIT_WARM = 1 } pararnn_init_mode;
 
 typedef struct {
-  int32_t max_iters;       /* Newton budget K, 1..PARARNN_MAX_ITERS                                 */
+  int32_t max_iters;       /* Newton budget K, 1..PARARNN_MAX_ITERS, or 0 = automatic: the measured
+                              K*(T) of pararnn_newton_budget for this cell, init_mode and T         */
   float tol;               /* <= 0: run exactly max_iters iterations.
                               > 0: iteration k evaluates R_k = max|r(H^k)| over b, t, d and state
                               components; the first iteration with R_k < tol is the last one (its
@@ -172,6 +173,20 @@ size_t pararnn_vjp_workspace_bytes(const pararnn_problem* prob);
 pararnn_status pararnn_scan_vjp(const pararnn_problem* prob, const float* s, const float* g,
                                 float* d_pre, float* d_w, float* d_bias, float* d_s0,
                                 float* lambda_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * pararnn_newton_budget -- (host only, no GPU call) the Newton budget a solve runs: max_iters when
+ * it is positive, else K*(T), the smallest K whose iterate agreed with the sequential unroll to 1e-4
+ * (max abs) in a measurement on a grid of lengths T (pararnn-torch README, "Benchmarks": the
+ * long-context K* campaign and the automatic iteration count; "Method" for the warm start).  The
+ * table was measured with the fp64 reference on seeded synthetic inputs (B = 1, D = 1024; gate
+ * inputs ~ N(0, 1), recurrent weights ~ U(-0.5, 0.5), biases ~ N(0, 0.01)); a length between grid
+ * points takes the next larger point's budget, a length beyond the grid one more than the last.
+ * LINEAR always needs 1.  It is a default for inputs like those, not a guarantee: tolerance mode
+ * (opts.tol > 0) is the guarantee.  A solve with an init_guess and max_iters = 0 uses the zero-start
+ * budget.  Returns K >= 1, or PARARNN_ERR_INVALID_ARG for a bad cell, init_mode, T or max_iters.
+ * ---------------------------------------------------------------------------------------------- */
+int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters);
 
 /* human-readable text of a status (static storage) */
 const char* pararnn_status_string(int status);

@@ -98,6 +98,8 @@ def load_library():
     lib.pararnn_newton_iterate.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     lib.pararnn_newton_report.restype = i32
     lib.pararnn_newton_report.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    lib.pararnn_newton_budget.restype = i32
+    lib.pararnn_newton_budget.argtypes = [i32, i32, i64, i32]
     lib.pararnn_scan_workspace_bytes.restype = sz
     lib.pararnn_scan_workspace_bytes.argtypes = [i32, i64, i64, i64]
     lib.pararnn_linear_scan.restype = i32
@@ -181,11 +183,21 @@ def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
     return int(load_library().pararnn_newton_workspace_bytes(ctypes.byref(st), None))
 
 
+def newton_budget(cell, T, warm_start=False, max_iters=None) -> int:
+    """The Newton budget a solve runs: max_iters, or the measured K*(T) when it is None or 0."""
+    c = CELLS[cell] if isinstance(cell, str) else int(cell)
+    k = load_library().pararnn_newton_budget(c, INIT_WARM if warm_start else INIT_ZERO, int(T), int(max_iters or 0))
+    if k < 1:
+        raise PararnnError(k, "pararnn_newton_budget")
+    return k
+
+
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
                  final_residual=False, report=True, on_iteration=None, warm_start=False):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
+    max_iters None or 0: the measured budget K*(T) (see newton_budget).
     tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
     (evaluated at its input iterate) is below tol.  report=True waits for the stream.
     warm_start: without init_guess, start from H^0_t = f(0, x_t) instead of zeros.
@@ -204,7 +216,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
         raise ValueError("out must be [S, B, T, D]")
     if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
         raise ValueError("init_guess must be [S, B, T, D]")
-    opts = _Opts(int(max_iters), float(tol), init_guess.data_ptr() if init_guess is not None else None,
+    opts = _Opts(int(max_iters or 0), float(tol), init_guess.data_ptr() if init_guess is not None else None,
                  1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO)
     nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
     ws = _workspace(nbytes, dev, "newton")
@@ -215,7 +227,8 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
                                       stream, ctypes.byref(rep) if rep is not None else None)
     else:
         rc = lib.pararnn_newton_prepare(ctypes.byref(st), ctypes.byref(opts), _ptr(ws), ws.numel(), stream)
-        for k in range(int(max_iters)):
+        K = newton_budget(cell, T, warm_start and init_guess is None, max_iters)
+        for k in range(K):
             if rc != 0:
                 break
             on_iteration(k, "before")

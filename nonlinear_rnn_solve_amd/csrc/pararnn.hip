@@ -1571,11 +1571,48 @@ size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_n
 
 namespace {
 // common validation of the Newton entry points; `need_out` checks s_out as well
+// Newton budget K*(T): the smallest iteration count whose iterate agreed with the sequential unroll
+// to 1e-4 (max abs) on the seeded synthetic inputs of the benchmark workloads (B = 1, D = 1024; GRU
+// with bf16 gate inputs, LSTM fp32), per first iterate, measured on a grid of lengths with the fp64
+// oracle -- the protocol of the pararnn-torch README's long-context campaign ("Benchmarks").  A
+// length between grid points takes the next larger point's budget; beyond the grid, one more.
+struct KStarRow { int32_t cell, init; int64_t T; int32_t k; };
+constexpr KStarRow kKStar[] = {
+    {CELL_GRU, PARARNN_INIT_ZERO, 1024, 3}, {CELL_GRU, PARARNN_INIT_WARM, 1024, 3},
+    {CELL_GRU, PARARNN_INIT_ZERO, 4096, 3}, {CELL_GRU, PARARNN_INIT_WARM, 4096, 3},
+    {CELL_GRU, PARARNN_INIT_ZERO, 16384, 3}, {CELL_GRU, PARARNN_INIT_WARM, 16384, 3},
+    {CELL_GRU, PARARNN_INIT_ZERO, 65536, 3}, {CELL_GRU, PARARNN_INIT_WARM, 65536, 3},
+    {CELL_GRU, PARARNN_INIT_ZERO, 131072, 3}, {CELL_GRU, PARARNN_INIT_WARM, 131072, 3},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 1024, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 1024, 4},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 4096, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 4096, 4},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 16384, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 16384, 4},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 65536, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 65536, 4},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 131072, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 131072, 4},
+};
+
+int auto_iters(int cell, int init, int64_t T) {
+  if (cell == CELL_LINEAR) return 1;  // one scan is exact
+  int last = 0;
+  for (const KStarRow& r : kKStar) {
+    if (r.cell != cell || r.init != init) continue;
+    if (T <= r.T) return r.k;
+    last = r.k;
+  }
+  return last + 1;
+}
+
+// the budget a solve runs: max_iters, or K*(T) when max_iters is 0 (a caller-supplied first
+// iterate counts as the zero start: nothing is known about its quality)
+int budget(const pararnn_problem* pb, const pararnn_newton_opts* op) {
+  if (op->max_iters > 0) return op->max_iters;
+  return auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T);
+}
+
 pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
                             bool need_out, void* ws, size_t ws_bytes) {
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
-  if (!op || op->max_iters < 1 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (!op || op->max_iters < 0 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
   if (op->init_mode != PARARNN_INIT_ZERO && op->init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
@@ -1596,7 +1633,7 @@ pararnn_status pararnn_newton_iterate(const pararnn_problem* pb, const pararnn_n
                                       void* ws, size_t ws_bytes, void* stream) {
   pararnn_status rc = newton_check(pb, op, s_out, true, ws, ws_bytes);
   if (rc || problem_N(pb) == 0) return rc;
-  if (k < 0 || k >= op->max_iters) return PARARNN_ERR_INVALID_ARG;
+  if (k < 0 || k >= budget(pb, op)) return PARARNN_ERR_INVALID_ARG;
   return pick_newton(pb->cell, pb->pre_dtype).iterate(pb, op, k, s_out, ws, static_cast<hipStream_t>(stream));
 }
 
@@ -1619,9 +1656,10 @@ pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_ne
   if (hipMemcpyAsync(res, static_cast<char*>(ws) + kResOffset, sizeof(res), hipMemcpyDeviceToHost, st) != hipSuccess)
     return PARARNN_ERR_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return PARARNN_ERR_HIP;
-  int iters = op->max_iters, conv = 0;
+  const int K = budget(pb, op);
+  int iters = K, conv = 0;
   pararnn_status out = PARARNN_OK;
-  for (int k = 0; k < op->max_iters; ++k) {
+  for (int k = 0; k < K; ++k) {
     float r;
     std::memcpy(&r, &res[k], sizeof r);
     report->residual[k] = r;
@@ -1630,7 +1668,7 @@ pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_ne
       if (r < op->tol) { iters = k + 1; conv = 1; break; }
     }
   }
-  for (int k = iters; k < op->max_iters; ++k) report->residual[k] = 0.0f;
+  for (int k = iters; k < K; ++k) report->residual[k] = 0.0f;
   report->iters = iters;
   report->converged = conv;
   report->n_residual = iters;
@@ -1651,10 +1689,18 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
   const NewtonEntry ne = pick_newton(pb->cell, pb->pre_dtype);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = ne.prepare(pb, ws, st);
-  for (int k = 0; k < op->max_iters && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+  const int K = budget(pb, op);
+  for (int k = 0; k < K && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
   if (rc) return rc;
   if (!report && !op->final_residual) return PARARNN_OK;
   return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
+}
+
+int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {
+  if (cell < CELL_LINEAR || cell > CELL_LSTM || T < 0 || max_iters < 0 || max_iters > PARARNN_MAX_ITERS)
+    return PARARNN_ERR_INVALID_ARG;
+  if (init_mode != PARARNN_INIT_ZERO && init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
+  return max_iters > 0 ? max_iters : auto_iters(cell, init_mode, T);
 }
 
 size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {

@@ -2,6 +2,7 @@
 header declares, the Python binding's struct layouts match the header, and argument validation
 returns the documented status codes before anything is launched."""
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -28,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True, text=True).stdout
@@ -94,7 +95,7 @@ def test_validation_codes_without_launching(lib):
     p = _problem()
     p.pre[0] = 4097                                         # misaligned
     assert solve(p) == -1
-    assert solve(_problem(), o=api._Opts(0, 0.0, None, 0)) == -1
+    assert solve(_problem(), o=api._Opts(-1, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
     assert solve(_problem(), w=ctypes.c_void_p(0)) == -3
@@ -127,3 +128,27 @@ def test_binding_refuses_cpu_tensors():
     a = torch.zeros(1, 8, 4)
     with pytest.raises(ValueError, match="GPU tensor"):
         api.linear_scan(a, a)
+
+
+def test_automatic_budget_is_the_measured_kstar(lib):
+    # the library's K*(T) table must be the one the oracle campaign measured (tests/golden/kstar.json)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kstar.json")) as f:
+        gold = json.load(f)
+    grid = gold["t_grid"]
+    for e in gold["entries"]:
+        c, init = api.CELLS[e["cell"]], 1 if e["init"] == "warm" else 0
+        assert e["kstar"] is not None
+        assert lib.pararnn_newton_budget(c, init, e["T"], 0) == e["kstar"], e
+        # between grid points: the next larger point's budget; beyond the grid: one more
+        i = grid.index(e["T"])
+        lo = grid[i - 1] + 1 if i else 1
+        assert lib.pararnn_newton_budget(c, init, lo, 0) == e["kstar"]
+        if e["T"] == grid[-1]:
+            assert lib.pararnn_newton_budget(c, init, grid[-1] + 1, 0) == e["kstar"] + 1
+    assert lib.pararnn_newton_budget(0, 0, 10 ** 9, 0) == 1          # LINEAR: one exact scan
+    assert lib.pararnn_newton_budget(1, 0, 100, 5) == 5              # an explicit budget wins
+    assert lib.pararnn_newton_budget(1, 2, 100, 0) == -1
+    assert lib.pararnn_newton_budget(3, 0, 100, 0) == -1
+    assert lib.pararnn_newton_budget(1, 0, -1, 0) == -1
+    assert lib.pararnn_newton_budget(1, 0, 100, 65) == -1
+    assert api.newton_budget("gru", 4096) == lib.pararnn_newton_budget(1, 0, 4096, 0)

@@ -342,3 +342,33 @@ def test_full_config4_newton_tol_and_vjp():
     e_dw = np.max(np.abs(gr["d_w"].cpu().numpy()[:, ds] - ref["d_w"]) / (1 + np.abs(ref["d_w"])))
     print("  vjp lambda", e_lam, "d_pre", e_dp, "d_w", e_dw)
     assert e_lam <= 2e-2 and e_dp <= 2e-2 and e_dw <= 2e-2
+
+
+# ------------------------------------------------------------------------------------------------
+# automatic budget K*(T) (max_iters = 0): the measured table against the sequential unroll
+# ------------------------------------------------------------------------------------------------
+def _kstar_gold():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kstar.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("cell,T,warm", [("gru", 16384, False), ("gru", 16384, True), ("lstm", 4096, False),
+                                         ("lstm", 16384, True), ("gru", 131072, False), ("lstm", 131072, True)])
+def test_automatic_budget_meets_the_agreement_tolerance(cell, T, warm):
+    gold = _kstar_gold()
+    e = [x for x in gold["entries"] if x["cell"] == cell and x["T"] == T and x["init"] == ("warm" if warm else "zero")][0]
+    announce("auto budget", cell, T, "warm" if warm else "zero", "K*", e["kstar"])
+    inp = synth.make_inputs(cell, gold["B"], T, gold["D"], dtype=e["dtype"], seed=e["seed"])
+    got, rep = api.newton_solve(cell, dev_pre(inp), dev(inp.w), dev(inp.bias), max_iters=None, warm_start=warm)
+    assert rep.iters == e["kstar"] == api.newton_budget(cell, T, warm)
+    # the full trajectory up to 16384 steps, sampled channels beyond
+    ch = None if T <= 16384 else sample_channels(gold["B"], gold["D"], 24, seed=5)
+    prob = oracle_problem(inp, channels=ch)
+    g = got.cpu().numpy() if ch is None else take_channels(got.cpu().numpy(), ch)
+    err_unroll = max_abs(g, oracle.unroll(prob))
+    err_iter = max_abs(g, oracle.newton(prob, e["kstar"], warm=warm)[0])
+    print("  vs unroll", err_unroll, "vs oracle iterate", err_iter)
+    assert err_iter <= 1e-5
+    assert err_unroll <= gold["tau"] + 1e-5
