@@ -64,9 +64,9 @@ def _load():
         lib.or_unroll.argtypes = [vp, vp, i32]
         lib.or_residual.argtypes = [vp, vp, vp, i32]
         lib.or_newton.argtypes = [vp, vp, i32, i32, dbl, vp, vp, vp, vp, i32]
-        lib.or_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, i32, vp, i32]
+        lib.or_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, i32]
         lib.or_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        assert lib.or_abi_version() == 4
+        assert lib.or_abi_version() == 5
         _lib = lib
     return _lib
 
@@ -75,7 +75,7 @@ class _Problem(ctypes.Structure):
     _fields_ = [("cell", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("pre", ctypes.c_void_p * 4), ("w", ctypes.c_void_p),
-                ("bias", ctypes.c_void_p), ("s0", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("s0", ctypes.c_void_p), ("seg_start", ctypes.c_void_p)]
 
 
 def default_threads() -> int:
@@ -84,6 +84,18 @@ def default_threads() -> int:
 
 def _ptr(a):
     return None if a is None else a.ctypes.data
+
+
+def seg_start_flags(cu_seqlens, T):
+    """Packed sequences: offsets cu_seqlens (sequence j covers steps cu[j] .. cu[j+1]-1) -> a [T]
+    uint8 array that is 1 where a sequence other than the first begins.  None -> None."""
+    if cu_seqlens is None:
+        return None
+    flags = np.zeros(max(T, 1), np.uint8)
+    for c in np.asarray(cu_seqlens).ravel():
+        if 0 < int(c) < T:
+            flags[int(c)] = 1
+    return flags
 
 
 def _as_pre(pre, dtype):
@@ -95,7 +107,7 @@ def _as_pre(pre, dtype):
 class Problem:
     """Holds contiguous copies of the inputs and the ctypes struct that points at them."""
 
-    def __init__(self, cell, pre, w=None, bias=None, s0=None, dtype=F32):
+    def __init__(self, cell, pre, w=None, bias=None, s0=None, dtype=F32, cu_seqlens=None):
         cell = CELLS.get(cell, cell)
         self.cell, self.dtype = cell, dtype
         self.pre = _as_pre(pre, dtype)
@@ -116,6 +128,8 @@ class Problem:
         for g in range(4):
             st.pre[g] = _ptr(self.pre[g]) if g < G else None
         st.w, st.bias, st.s0 = _ptr(self.w), _ptr(self.bias), _ptr(self.s0)
+        self.seg_start = seg_start_flags(cu_seqlens, T)
+        st.seg_start = _ptr(self.seg_start)
         self.struct = st
 
     def traj_shape(self):
@@ -172,7 +186,7 @@ def newton(prob: Problem, max_iters, tol=0.0, init_guess=None, nthreads=None, wa
     return H, res[: it.value].copy(), it.value, bool(conv.value), rc
 
 
-def linear_scan(a, b, s0=None, reverse=False, S=1, dtype=F32, nthreads=None):
+def linear_scan(a, b, s0=None, reverse=False, S=1, dtype=F32, nthreads=None, cu_seqlens=None):
     """Sequential linear recurrence in fp64. S=1: a,b [B][T][D]; S=2: a [4][B][T][D], b [2][B][T][D]."""
     want = np.float32 if dtype == F32 else np.uint16
     a = np.ascontiguousarray(a, dtype=want)
@@ -184,7 +198,8 @@ def linear_scan(a, b, s0=None, reverse=False, S=1, dtype=F32, nthreads=None):
         assert a.shape == (B, T, D) and b.shape == (B, T, D)
     s0a = None if s0 is None else np.ascontiguousarray(s0, dtype=np.float32).reshape(S, B, D)
     out = np.zeros((S, B, T, D) if S == 2 else (B, T, D), dtype=np.float64)
-    _check(_load().or_linear_scan(S, B, T, D, dtype, _ptr(a), _ptr(b), _ptr(s0a), 1 if reverse else 0,
+    seg = seg_start_flags(cu_seqlens, T)
+    _check(_load().or_linear_scan(S, B, T, D, dtype, _ptr(a), _ptr(b), _ptr(s0a), _ptr(seg), 1 if reverse else 0,
                                   _ptr(out), nthreads or default_threads()), "linear_scan")
     return out
 

@@ -164,6 +164,9 @@ typedef struct {
   const float* w;      /* [G][D] (GRU, LSTM)  */
   const float* bias;   /* [G][D] (GRU, LSTM)  */
   const float* s0;     /* [S][B][D] or NULL (zeros) */
+  const unsigned char* seg_start; /* [T] or NULL: nonzero where a new packed sequence begins
+                                     (that step's previous state is zero; s0 is the first
+                                     sequence's initial state)                              */
 } or_problem;
 
 static int64_t elem_index(const or_problem* p, int64_t b, int64_t t, int64_t d) {
@@ -191,9 +194,22 @@ static void gather_s0(const or_problem* p, int64_t b, int64_t d, double* s) {
     s[k] = p->s0 ? (double)p->s0[(k * p->B + b) * p->D + d] : 0.0;
 }
 
+/* does step t begin a new packed sequence (t > 0)? */
+static int starts_at(const or_problem* p, int64_t t) { return t > 0 && p->seg_start && p->seg_start[t]; }
+
+/* the state step t starts from: s0 at t = 0, zero where a new sequence begins, else H_{t-1} */
+static void prev_state(const or_problem* p, const double* H, int64_t b, int64_t t, int64_t d, double* prev);
+
 /* state plane k of a trajectory laid out [S][B][T][D] */
 static int64_t traj_index(const or_problem* p, int k, int64_t b, int64_t t, int64_t d) {
   return ((k * p->B + b) * p->T + t) * p->D + d;
+}
+
+static void prev_state(const or_problem* p, const double* H, int64_t b, int64_t t, int64_t d, double* prev) {
+  int S = state_size(p->cell);
+  if (t == 0) gather_s0(p, b, d, prev);
+  else if (starts_at(p, t)) for (int k = 0; k < S; ++k) prev[k] = 0.0;
+  else for (int k = 0; k < S; ++k) prev[k] = H[traj_index(p, k, b, t - 1, d)];
 }
 
 /* ------------------------------------------------------------------------ */
@@ -267,6 +283,7 @@ static void unroll_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     gather_params(p, d, w, bias);
     gather_s0(p, b, d, s);
     for (int64_t t = 0; t < p->T; ++t) {
+      if (starts_at(p, t)) for (int k = 0; k < S; ++k) s[k] = 0.0;
       gather_u(p, b, t, d, u);
       or_cell_step(p->cell, u, w, bias, s, sn, NULL, NULL, NULL);
       for (int k = 0; k < S; ++k) {
@@ -306,8 +323,7 @@ static void resid_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
     for (int64_t t = 0; t < p->T; ++t) {
-      if (t == 0) gather_s0(p, b, d, prev);
-      else for (int k = 0; k < S; ++k) prev[k] = c->H[traj_index(p, k, b, t - 1, d)];
+      prev_state(p, c->H, b, t, d, prev);
       gather_u(p, b, t, d, u);
       or_cell_step(p->cell, u, w, bias, prev, sn, NULL, NULL, NULL);
       for (int k = 0; k < S; ++k) m = nan_max(m, fabs(c->H[traj_index(p, k, b, t, d)] - sn[k]));
@@ -335,7 +351,8 @@ int or_residual(const or_problem* p, const double* H, double* out_max, int nthre
 /* Newton on F(H) = 0 (pararnn-torch README, "Method")                       */
 /* ------------------------------------------------------------------------ */
 /*
- * Iteration k, at the current trajectory H^k (H^k_{-1} := s0):
+ * Iteration k, at the current trajectory H^k (H^k_{-1} := s0; with packed
+ * sequences the step before each later sequence's first is the zero state):
  *   r_t = h^k_t - f(h^k_{t-1}, x_t)                       (residual)
  *   J_t = d f / d s  at (h^k_{t-1}, x_t)                  (Jacobian)
  *   R_k = max |r_t|                                      (max residual)
@@ -371,10 +388,11 @@ static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     gather_params(p, d, w, bias);
     /* residual and Jacobian at the current iterate */
     for (int64_t t = 0; t < T; ++t) {
-      if (t == 0) gather_s0(p, b, d, prev);
-      else for (int k = 0; k < S; ++k) prev[k] = c->H[traj_index(p, k, b, t - 1, d)];
+      prev_state(p, c->H, b, t, d, prev);
       gather_u(p, b, t, d, u);
       or_cell_step(p->cell, u, w, bias, prev, sn, J + t * S * S, NULL, NULL);
+      /* where a sequence begins, h_{t-1} does not enter f: that step's Jacobian is zero */
+      if (starts_at(p, t)) for (int k = 0; k < S * S; ++k) J[t * S * S + k] = 0.0;
       for (int k = 0; k < S; ++k) {
         r[t * S + k] = c->H[traj_index(p, k, b, t, d)] - sn[k];
         m = nan_max(m, fabs(r[t * S + k]));
@@ -397,18 +415,26 @@ static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
 
 /* warm start (pararnn-torch README, "Method": the GRU/LSTM first iterate is the cell applied to a
    zero previous state): H^0_t = f(0, x_t) for every t */
-static void warm_start(const or_problem* p, double* H) {
+typedef struct {
+  const or_problem* p;
+  double* H;
+} warm_ctx;
+
+static void warm_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
+  (void)worker;
+  warm_ctx* c = (warm_ctx*)vctx;
+  const or_problem* p = c->p;
   int S = state_size(p->cell);
   double u[4], w[4], bias[4], zero[2] = {0.0, 0.0}, sn[2];
-  for (int64_t b = 0; b < p->B; ++b)
-    for (int64_t d = 0; d < p->D; ++d) {
-      gather_params(p, d, w, bias);
-      for (int64_t t = 0; t < p->T; ++t) {
-        gather_u(p, b, t, d, u);
-        or_cell_step(p->cell, u, w, bias, zero, sn, NULL, NULL, NULL);
-        for (int k = 0; k < S; ++k) H[traj_index(p, k, b, t, d)] = sn[k];
-      }
+  for (int64_t ch = ch0; ch < ch1; ++ch) {
+    int64_t b = ch / p->D, d = ch % p->D;
+    gather_params(p, d, w, bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      gather_u(p, b, t, d, u);
+      or_cell_step(p->cell, u, w, bias, zero, sn, NULL, NULL, NULL);
+      for (int k = 0; k < S; ++k) c->H[traj_index(p, k, b, t, d)] = sn[k];
     }
+  }
 }
 
 /* init_mode: 0 = init_guess or zeros, 1 = warm start (ignored when init_guess is given) */
@@ -420,8 +446,12 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int m
   int S = state_size(p->cell);
   int64_t n = (int64_t)S * p->B * p->T * p->D;
   for (int64_t i = 0; i < n; ++i) H[i] = init_guess ? (double)init_guess[i] : 0.0;
-  if (!init_guess && init_mode == 1) warm_start(p, H);
   if (nthreads < 1) nthreads = 1;
+  if (!init_guess && init_mode == 1) {
+    warm_ctx wc = {p, H};
+    rc = run_channels(p->B * p->D, nthreads, warm_channels, &wc);
+    if (rc) return rc;
+  }
   double* wm = (double*)malloc(sizeof(double) * (size_t)nthreads);
   double* scratch = (double*)malloc(sizeof(double) * (size_t)nthreads *
                                     (size_t)(p->T > 0 ? p->T : 1) * (size_t)(2 * S + S * S));
@@ -452,6 +482,8 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int m
 /*
  * forward:  s_{-1} = s0,  s_t = A_t s_{t-1} + b_t,  t = 0..T-1
  * reverse:  s_T    = s0,  s_t = A_t s_{t+1} + b_t,  t = T-1..0
+ * With packed sequences (seg_start[t] set where one begins), s_{t-1} (forward)
+ * or s_{t+1} (reverse) is zero across each boundary between sequences.
  * S = 1: a is [B][T][D], b is [B][T][D].
  * S = 2: a is [4][B][T][D] (A00, A01, A10, A11 row-major), b is [2][B][T][D].
  * This is the recurrence that every Newton linear solve reduces to
@@ -465,6 +497,7 @@ typedef struct {
   const void* a;
   const void* b;
   const float* s0;
+  const unsigned char* seg_start;
   double* out;
 } lin_ctx;
 
@@ -479,6 +512,10 @@ static void lin_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     for (int64_t step = 0; step < c->T; ++step) {
       int64_t t = c->reverse ? c->T - 1 - step : step;
       int64_t i = (b * c->T + t) * c->D + d;
+      /* packed sequences: the state entering a sequence's first step (forward) or last step
+         (reverse) is zero */
+      int64_t edge = c->reverse ? t + 1 : t;
+      if (c->seg_start && edge > 0 && edge < c->T && c->seg_start[edge]) s[0] = s[1] = 0.0;
       if (c->S == 1) {
         s[0] = load_in(c->a, c->dtype, i) * s[0] + load_in(c->b, c->dtype, i);
         c->out[i] = s[0];
@@ -497,10 +534,11 @@ static void lin_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
 }
 
 int or_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void* a,
-                   const void* b, const float* s0, int reverse, double* out, int nthreads) {
+                   const void* b, const float* s0, const unsigned char* seg_start, int reverse,
+                   double* out, int nthreads) {
   if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return OR_EINVAL;
   if (dtype != OR_F32 && dtype != OR_BF16) return OR_EINVAL;
-  lin_ctx c = {S, dtype, reverse ? 1 : 0, B, T, D, a, b, s0, out};
+  lin_ctx c = {S, dtype, reverse ? 1 : 0, B, T, D, a, b, s0, seg_start, out};
   return run_channels(B * D, nthreads, lin_channels, &c);
 }
 
@@ -518,6 +556,8 @@ int or_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void
  *   dL/dbias_gate  = sum_{b,t} dL/du_{gate,t}
  *   dL/ds0         = J_0^T lambda_0,  J_0 = d f/d s at (s0, x_0)
  * LINEAR: dL/da_t = lambda_t h_{t-1}, dL/db_t = lambda_t, dL/ds0 = a_0 lambda_0.
+ * Packed sequences: J_{t+1} is taken as zero where step t+1 begins a sequence
+ * (no adjoint flows back across it), and s_{t-1} is zero at such a step.
  * e_h is the unit vector of h (for the LSTM state (c, h), e_h = (0, 1)).
  * Sums over (b, t) are accumulated in plain sequential order per channel.
  */
@@ -548,7 +588,7 @@ static void vjp_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     for (int64_t t = T - 1; t >= 0; --t) {
       double acc[2] = {0.0, 0.0};
       acc[S - 1] = (double)c->g[elem_index(p, b, t, d)]; /* e_h g_t */
-      if (t + 1 < T) {
+      if (t + 1 < T && !starts_at(p, t + 1)) {   /* nothing flows back across a sequence start */
         for (int k = 0; k < S; ++k) prev[k] = c->s[traj_index(p, k, b, t, d)];
         gather_u(p, b, t + 1, d, u);
         or_cell_step(p->cell, u, w, bias, prev, sn, J, NULL, NULL);
@@ -560,8 +600,7 @@ static void vjp_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
     /* gate gradients and parameter sums, forwards in time */
     double wsum[4] = {0, 0, 0, 0}, bsum[4] = {0, 0, 0, 0};
     for (int64_t t = 0; t < T; ++t) {
-      if (t == 0) gather_s0(p, b, d, prev);
-      else for (int k = 0; k < S; ++k) prev[k] = c->s[traj_index(p, k, b, t - 1, d)];
+      prev_state(p, c->s, b, t, d, prev);
       gather_u(p, b, t, d, u);
       or_cell_step(p->cell, u, w, bias, prev, sn, J, dfdu, wcoef);
       for (int gi = 0; gi < G; ++gi) {
@@ -625,4 +664,4 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
 }
 
 /* ABI version of this file's entry points, so the wrapper can check it */
-int or_abi_version(void) { return 4; }
+int or_abi_version(void) { return 5; }

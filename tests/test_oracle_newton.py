@@ -31,8 +31,9 @@ def _fp64_default():
     torch.set_default_dtype(old)
 
 
-def dense_F(inp, s0):
-    """F(H)_t = s_t - f(s_{t-1}, x_t) on the flattened trajectory, built from the torch library cells."""
+def dense_F(inp, s0, starts=()):
+    """F(H)_t = s_t - f(s_{t-1}, x_t) on the flattened trajectory, built from the torch library cells.
+    starts: steps where a new packed sequence begins (their s_{t-1} is the zero state)."""
     B, T, D, S = inp.B, inp.T, inp.D, inp.S
     pre = [torch.tensor(p.astype(np.float64)) for p in inp.pre_f32()]
     s0t = torch.tensor(s0.astype(np.float64))
@@ -46,7 +47,7 @@ def dense_F(inp, s0):
         H = flat.reshape(S, B, T, D)
         out = []
         for t in range(T):
-            prev = s0t if t == 0 else H[:, :, t - 1, :]
+            prev = s0t if t == 0 else (torch.zeros_like(s0t) if t in starts else H[:, :, t - 1, :])
             x = torch.cat([p[:, t, :] for p in pre], 1)
             if S == 1:
                 f = cell(x, prev[0])[None]
@@ -58,10 +59,10 @@ def dense_F(inp, s0):
     return F
 
 
-def dense_newton(inp, s0, K):
+def dense_newton(inp, s0, K, starts=()):
     """Newton on the stacked system with an explicit Jacobian; returns the K-th iterate [S][B][T][D]."""
     S, B, T, D = inp.S, inp.B, inp.T, inp.D
-    F = dense_F(inp, s0)
+    F = dense_F(inp, s0, starts)
     H = torch.zeros(S * B * T * D)
     for _ in range(K):
         Jf = torch.autograd.functional.jacobian(F, H).numpy()

@@ -24,8 +24,9 @@ def _fp64_default():
     torch.set_default_dtype(old)
 
 
-def autograd_reference(inp, s0, g):
-    """Gradients of L = sum g * h through the sequential torch unroll."""
+def autograd_reference(inp, s0, g, starts=()):
+    """Gradients of L = sum g * h through the sequential torch unroll.  starts: steps where a new
+    packed sequence begins (the state entering them is replaced by zeros)."""
     B, T, D, S = inp.B, inp.T, inp.D, inp.S
     pre = [torch.tensor(p.astype(np.float64), requires_grad=True) for p in inp.pre_f32()]
     s0t = torch.tensor(s0.astype(np.float64), requires_grad=True)
@@ -35,6 +36,8 @@ def autograd_reference(inp, s0, g):
         h = s0t[0]
         hs = []
         for t in range(T):
+            if t in starts:
+                h = torch.zeros_like(h)
             h = a[:, t, :] * h + b[:, t, :]
             h.retain_grad()
             hs.append(h)
@@ -54,12 +57,16 @@ def autograd_reference(inp, s0, g):
     if S == 1:
         h = s0t[0]
         for t in range(T):
+            if t in starts:
+                h = torch.zeros_like(h)
             h = cell(torch.cat([p[:, t, :] for p in pre], 1), h)
             h.retain_grad()
             states.append([h])
     else:
         c, h = s0t[0], s0t[1]
         for t in range(T):
+            if t in starts:
+                c, h = torch.zeros_like(c), torch.zeros_like(h)
             h, c = cell(torch.cat([p[:, t, :] for p in pre], 1), (h, c))
             c.retain_grad()
             h.retain_grad()
