@@ -177,8 +177,8 @@ pararnn_status pararnn_scan_vjp(const pararnn_problem* prob, const float* s, con
 /* ------------------------------------------------------------------------------------------------
  * pararnn_newton_budget -- (host only, no GPU call) the Newton budget a solve runs: max_iters when
  * it is positive, else K*(T), the smallest K whose iterate agreed with the sequential unroll to 1e-4
- * (max abs) in a measurement on a grid of lengths T (pararnn-torch README, "Benchmarks": the
- * long-context K* campaign and the automatic iteration count; "Method" for the warm start).  The
+ * (max abs) in a measurement on a grid of lengths T (pararnn-torch README, "Method": K*(T) and
+ * the automatic iteration count; "Benchmarks": the tau = 1e-4, B = 1 campaign).  The
  * table was measured with the fp64 reference on seeded synthetic inputs (B = 1, D = 1024; gate
  * inputs ~ N(0, 1), recurrent weights ~ U(-0.5, 0.5), biases ~ N(0, 0.01)); a length between grid
  * points takes the next larger point's budget, a length beyond the grid one more than the last.

@@ -1574,7 +1574,8 @@ namespace {
 // Newton budget K*(T): the smallest iteration count whose iterate agreed with the sequential unroll
 // to 1e-4 (max abs) on the seeded synthetic inputs of the benchmark workloads (B = 1, D = 1024; GRU
 // with bf16 gate inputs, LSTM fp32), per first iterate, measured on a grid of lengths with the fp64
-// oracle -- the protocol of the pararnn-torch README's long-context campaign ("Benchmarks").  A
+// oracle -- K*(T) as the pararnn-torch README defines it ("Method") and measures it in its
+// long-context campaign ("Benchmarks").  A
 // length between grid points takes the next larger point's budget; beyond the grid, one more.
 struct KStarRow { int32_t cell, init; int64_t T; int32_t k; };
 constexpr KStarRow kKStar[] = {

@@ -2,9 +2,8 @@
 with the sequential unroll to tau = 1e-4 (max abs over every element and state component) -- for
 the diagonal GRU and LSTM, zero and warm first iterates, on a grid of sequence lengths.
 
-The protocol is the one the pararnn-torch README describes for its long-context campaign (section
-"Benchmarks": agreement tolerance 1e-4, B = 1, the measured budget labelled K*; "Method" for the
-warm start).  Inputs are the seeded synthetic ones of the benchmark workloads (GRU: bf16 gate
+The protocol is the one the pararnn-torch README describes: K*(T) and the warm start in section
+"Method", the long-context campaign (agreement tolerance 1e-4, B = 1) in section "Benchmarks".  Inputs are the seeded synthetic ones of the benchmark workloads (GRU: bf16 gate
 inputs, LSTM: fp32), B = 1, D = 1024.  Everything is computed by the fp64 CPU oracle: the iterates
 by Newton with sequential linear solves, the reference by the sequential unroll.
 

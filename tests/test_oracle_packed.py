@@ -1,5 +1,5 @@
-"""Pins for the oracle on packed variable-length sequences (pararnn-torch README, "Shapes and
-layout": packed batches described by cumulative sequence offsets, cu_seqlens).
+"""Pins for the oracle on packed variable-length sequences (pararnn-torch README, "Compatibility":
+shapes and packing, with packed batches described by cumulative sequence offsets, cu_seqlens).
 
 Reading: the [B][T][D] planes hold several sequences back to back along T; sequence j covers steps
 cu_seqlens[j] .. cu_seqlens[j+1]-1.  The state entering each sequence after the first is zero (s0
