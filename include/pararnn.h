@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PARARNN_ABI_VERSION 2
+#define PARARNN_ABI_VERSION 3
 /* upper bound of Newton iterations per call (report.residual holds one more) */
 #define PARARNN_MAX_ITERS 64
 
@@ -77,6 +77,14 @@ typedef struct {
   const float* w;        /* [G][D] diagonal recurrent weights (ignored for LINEAR)             */
   const float* bias;     /* [G][D] biases (ignored for LINEAR)                                 */
   const float* s0;       /* [S][B][D] initial state h_{-1}; NULL = zeros                        */
+  const int32_t* cu_seqlens; /* packed sequences, or NULL for one sequence per batch row: n_seqs+1
+                                nondecreasing offsets into T (device memory); sequence j covers steps
+                                cu_seqlens[j] .. cu_seqlens[j+1]-1 of every batch row.  The state
+                                entering each sequence after the first is zero (s0 is the first one's
+                                initial state) and nothing flows across a boundary, forward or in the
+                                VJP.  Only the offsets strictly between 0 and T matter; the library
+                                does not read them on the host, so it cannot check their order.    */
+  int64_t n_seqs;        /* number of packed sequences (ignored when cu_seqlens is NULL)          */
 } pararnn_problem;
 
 /* First Newton iterate when no init_guess is given.  WARM is the GRU / LSTM warm start of the
@@ -147,11 +155,15 @@ pararnn_status pararnn_newton_report(const pararnn_problem* prob, const pararnn_
  *   reverse (reverse = 1): s_T    = s0,  s_t = A_t s_{t+1} + b_t,  t = T-1 .. 0
  *   S = 1: a [B][T][D], b [B][T][D];  S = 2: a [4][B][T][D] (A00, A01, A10, A11), b [2][B][T][D].
  *   dtype: storage of a and b (fp32 or bf16).  s0 [S][B][D] fp32 or NULL (zeros).
+ *   cu_seqlens, n_seqs: packed sequences as in pararnn_problem, or NULL: the state entering each
+ *         sequence is zero, except s0 for the sequence at the scan's starting end (the first one
+ *         forward, the last one in reverse).
  *   s_out [S][B][T][D] fp32; it may alias a or b exactly (fp32 storage), not partially.
  * ---------------------------------------------------------------------------------------------- */
 size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D);
 pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype,
-                                   const void* a, const void* b, const float* s0, float* s_out,
+                                   const void* a, const void* b, const float* s0,
+                                   const int32_t* cu_seqlens, int64_t n_seqs, float* s_out,
                                    int reverse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------

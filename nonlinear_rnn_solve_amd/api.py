@@ -23,7 +23,7 @@ CELLS = {"linear": 0, "gru": 1, "lstm": 2}
 GATES = {0: 2, 1: 3, 2: 4}
 STATE = {0: 1, 1: 1, 2: 2}
 MAX_ITERS = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 INIT_ZERO, INIT_WARM = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
           -5: "Newton diverged"}
@@ -47,7 +47,7 @@ class _Problem(ctypes.Structure):
     _fields_ = [("cell", ctypes.c_int32), ("pre_dtype", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("pre", ctypes.c_void_p * 4), ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("s0", ctypes.c_void_p)]
+                ("s0", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int64)]
 
 
 class _Opts(ctypes.Structure):
@@ -64,7 +64,8 @@ class _Report(ctypes.Structure):
 class NewtonReport:
     iters: int
     converged: bool
-    residuals: list = field(default_factory=list)   # R_0 .. R_{iters-1} (+ final residual if asked)
+    residuals: list = field(default_factory=list)   # R_0 .. R_{iters-1}
+    # max residual of the returned trajectory (final_residual=True), else None
     final_residual: float | None = None
 
 
@@ -103,7 +104,7 @@ def load_library():
     lib.pararnn_scan_workspace_bytes.restype = sz
     lib.pararnn_scan_workspace_bytes.argtypes = [i32, i64, i64, i64]
     lib.pararnn_linear_scan.restype = i32
-    lib.pararnn_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.pararnn_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
     lib.pararnn_vjp_workspace_bytes.restype = sz
     lib.pararnn_vjp_workspace_bytes.argtypes = [vp]
     lib.pararnn_scan_vjp.restype = i32
@@ -147,7 +148,19 @@ def _workspace(nbytes: int, device, key: str):
     return buf
 
 
-def _problem(cell, pre, w, bias, s0):
+def _seqlens(cu_seqlens, device):
+    """Packed-sequence offsets: an int32 tensor [n_seqs + 1] on the GPU (or None)."""
+    if cu_seqlens is None:
+        return None, 0
+    _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of n_seqs + 1 offsets")
+    if cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be on the same device as the inputs")
+    return cu_seqlens.data_ptr(), cu_seqlens.numel() - 1
+
+
+def _problem(cell, pre, w, bias, s0, cu_seqlens=None):
     c = CELLS[cell] if isinstance(cell, str) else int(cell)
     G, S = GATES[c], STATE[c]
     if len(pre) != G:
@@ -175,11 +188,12 @@ def _problem(cell, pre, w, bias, s0):
     st.w = w.data_ptr() if (c != 0 and w is not None) else None
     st.bias = bias.data_ptr() if (c != 0 and bias is not None) else None
     st.s0 = s0.data_ptr() if s0 is not None else None
+    st.cu_seqlens, st.n_seqs = _seqlens(cu_seqlens, pre[0].device)
     return st, c, G, S, (B, T, D)
 
 
-def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
-    st, *_ = _problem(cell, pre, w, bias, s0)
+def newton_workspace_bytes(cell, pre, w=None, bias=None, s0=None, cu_seqlens=None) -> int:
+    st, *_ = _problem(cell, pre, w, bias, s0, cu_seqlens)
     return int(load_library().pararnn_newton_workspace_bytes(ctypes.byref(st), None))
 
 
@@ -193,7 +207,7 @@ def newton_budget(cell, T, warm_start=False, max_iters=None) -> int:
 
 
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
-                 final_residual=False, report=True, on_iteration=None, warm_start=False):
+                 final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
@@ -201,12 +215,14 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
     (evaluated at its input iterate) is below tol.  report=True waits for the stream.
     warm_start: without init_guess, start from H^0_t = f(0, x_t) instead of zeros.
+    cu_seqlens: int32 [n_seqs + 1] offsets of sequences packed along T (every batch row); each sequence
+    after the first starts from the zero state.
     on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
     launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
     entry points prepare / iterate / report, which launch exactly the same kernels.
     """
     lib = load_library()
-    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0)
+    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0, cu_seqlens)
     dev = pre[0].device
     if out is None:
         out = torch.empty((S, B, T, D), dtype=torch.float32, device=dev)
@@ -241,7 +257,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     r = None
     if rep is not None:
         res = [float(rep.residual[i]) for i in range(rep.n_residual)]
-        r = NewtonReport(int(rep.iters), bool(rep.converged), res,
+        r = NewtonReport(int(rep.iters), bool(rep.converged), res[:rep.iters],
                          res[rep.iters] if final_residual and rep.n_residual > rep.iters else None)
     if rc == -5:
         raise NewtonDivergenceError(rc, "pararnn_newton_solve", r)
@@ -254,11 +270,13 @@ def scan_workspace_bytes(S, B, T, D) -> int:
     return int(load_library().pararnn_scan_workspace_bytes(S, B, T, D))
 
 
-def linear_scan(a, b, s0=None, reverse=False, out=None):
+def linear_scan(a, b, s0=None, reverse=False, out=None, cu_seqlens=None):
     """Single-pass parallel linear recurrence.
 
     S=1: a, b [B, T, D];  S=2: a [4, B, T, D] (A00, A01, A10, A11), b [2, B, T, D].
     forward: s_t = A_t s_{t-1} + b_t (s_{-1} = s0);  reverse: s_t = A_t s_{t+1} + b_t (s_T = s0).
+    cu_seqlens: int32 [n_seqs + 1] offsets of packed sequences; the state entering each is zero, s0
+    entering the one at the scan's starting end.
     Returns float32 [B, T, D] (S=1) or [2, B, T, D] (S=2).
     """
     lib = load_library()
@@ -280,27 +298,30 @@ def linear_scan(a, b, s0=None, reverse=False, out=None):
     _check_dev(out, "out", torch.float32)
     if out.shape != b.shape:
         raise ValueError("out must have b's shape")
+    cu, n_seqs = _seqlens(cu_seqlens, a.device)
     nbytes = lib.pararnn_scan_workspace_bytes(S, B, T, D)
     ws = _workspace(nbytes, a.device, "scan")
     rc = lib.pararnn_linear_scan(S, B, T, D, 1 if a.dtype == torch.bfloat16 else 0, _ptr(a), _ptr(b), _ptr(s0),
-                                 _ptr(out), 1 if reverse else 0, _ptr(ws), ws.numel(), _stream(a.device))
+                                 cu, n_seqs, _ptr(out), 1 if reverse else 0, _ptr(ws), ws.numel(),
+                                 _stream(a.device))
     if rc != 0:
         raise PararnnError(rc, "pararnn_linear_scan")
     return out
 
 
-def vjp_workspace_bytes(cell, pre, w=None, bias=None, s0=None) -> int:
-    st, *_ = _problem(cell, pre, w, bias, s0)
+def vjp_workspace_bytes(cell, pre, w=None, bias=None, s0=None, cu_seqlens=None) -> int:
+    st, *_ = _problem(cell, pre, w, bias, s0, cu_seqlens)
     return int(load_library().pararnn_vjp_workspace_bytes(ctypes.byref(st)))
 
 
-def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, want_params=True, want_s0=True):
+def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, want_params=True, want_s0=True,
+             cu_seqlens=None):
     """Gradients at trajectory s ([S,B,T,D] float32) for upstream g = dL/dh ([B,T,D] float32).
 
     Returns dict: d_pre [G,B,T,D]; d_w, d_bias [G,D] (gated cells); d_s0 [S,B,D]; lam [S,B,T,D] if asked.
     """
     lib = load_library()
-    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0)
+    st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0, cu_seqlens)
     dev = pre[0].device
     _check_dev(s, "s", torch.float32)
     _check_dev(g, "g", torch.float32)

@@ -213,12 +213,23 @@ DEV float word_val(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)
 
 struct Common {
   uint64_t* lb;         // look-back words
+  const uint32_t* seg;  // packed sequences: bit t set where a sequence other than the first begins
   uint32_t* ticket;     // tile ticket counter of this launch (zeroed before the launch)
   uint32_t tag;         // nonzero tag of this launch
   int32_t n_chains;     // channel tiles
   int64_t n_chunks;     // time chunks
   int64_t T, D, C, N;   // time steps, channels per row, B*D channels, B*T*D elements
 };
+
+// Packed sequences: 32 mask bits starting at step t0 (bit i <-> step t0 + i).  The mask has
+// (T >> 5) + 2 words and no bit at or past T, so the two words read are in bounds for any
+// t0 <= T; lanes whose steps lie past T read some in-bounds word and mask those steps anyway.
+DEV uint32_t seg_bits(const uint32_t* seg, int64_t t0, int64_t T) {
+  const int64_t tc = t0 < T ? t0 : T;
+  const int64_t w = tc >> 5;
+  const uint64_t win = (static_cast<uint64_t>(seg[w + 1]) << 32) | seg[w];
+  return static_cast<uint32_t>(win >> (tc & 31));
+}
 
 // A tile is TW channels x CT steps.  A wave's 64 lanes form TS time slices of 64/TS lanes; lane
 // (slice s, position j) owns channels [j*V, j*V+V) of the tile and L consecutive steps; the NW*TS
@@ -609,7 +620,7 @@ DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&
 // ------------------------------------------------------------------------------------------------
 // Op 1: linear recurrence (pararnn_linear_scan)
 // ------------------------------------------------------------------------------------------------
-template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_, int TS_>
+template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = REV, RESID = false;
@@ -651,14 +662,19 @@ struct LinearOp {
 #pragma unroll
       for (int k = 0; k < S; ++k) ldv<V, DT>(a.b, k * N + idx, bv[k][i]);
     }
+    // packed sequences: no state crosses into a sequence's first step (forward) or out of its
+    // first step into the previous sequence's last (reverse), so that step's A is zero
+    uint32_t sb = 0;
+    if constexpr (SEG) sb = seg_bits(a.c.seg, tl.t_lo + (REV ? 1 : 0), T);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const bool ok = !MASKED || i < tl.nvalid;
+      const bool rs = SEG && ((sb >> i) & 1u);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const Aff<S> one = aff_id<S>();
 #pragma unroll
-        for (int k = 0; k < S * S; ++k) ln.e[v][i].A[k] = ok ? av[k][i][v] : one.A[k];
+        for (int k = 0; k < S * S; ++k) ln.e[v][i].A[k] = ok ? (rs ? 0.0f : av[k][i][v]) : one.A[k];
 #pragma unroll
         for (int k = 0; k < S; ++k) ln.e[v][i].b[k] = ok ? bv[k][i][v] : 0.0f;
       }
@@ -691,7 +707,7 @@ struct LinearOp {
 //   r_t = h^k_t - f_t (the same iterate, written without forming delta).  The max |r_t| is
 //   reduced for the tolerance test.  LINEAR: the element is (a_t, b_t) itself.
 // ------------------------------------------------------------------------------------------------
-template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
@@ -840,32 +856,41 @@ struct NewtonOp {
           }
       }
     }
+    // packed sequences: a step that begins a sequence starts from the zero state, so its previous
+    // state is 0 and its Jacobian (the element's A) is zero
+    uint32_t sb = 0;
+    if constexpr (SEG) sb = seg_bits(c.seg, tl.t_lo, T);
     ResidMax rm;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const bool ok = !MASKED || i < tl.nvalid;
+      const bool rs = SEG && ((sb >> i) & 1u);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         Aff<S> e;
         if constexpr (CELL == CELL_LINEAR) {
-          const float f = fmaf(u[0][i][v], h[0][i][v], u[1][i][v]);
+          const float hp = rs ? 0.0f : h[0][i][v];
+          const float f = fmaf(u[0][i][v], hp, u[1][i][v]);
           if (ok) rm.add(h[0][i + 1][v] - f);
-          e.A[0] = u[0][i][v];
+          e.A[0] = rs ? 0.0f : u[0][i][v];
           e.b[0] = u[1][i][v];
         } else if constexpr (CELL == CELL_GRU) {
-          const float hp = h[0][i][v];
+          const float hp = rs ? 0.0f : h[0][i][v];
           const GruOut q = gru_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], hp);
           if (ok) rm.add(h[0][i + 1][v] - q.f);
-          e.A[0] = q.J;
+          e.A[0] = rs ? 0.0f : q.J;
           e.b[0] = fmaf(-q.J, hp, q.f);
         } else {
-          const float cp = h[0][i][v], hp = h[1][i][v];
+          const float cp = rs ? 0.0f : h[0][i][v], hp = rs ? 0.0f : h[1][i][v];
           const LstmPart q = lstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], cp, hp);
           if (ok) {
             rm.add(h[0][i + 1][v] - q.c2);
             rm.add(h[1][i + 1][v] - q.h2);
           }
-          e.A[0] = q.J00; e.A[1] = q.J01; e.A[2] = q.J10; e.A[3] = q.J11;
+          e.A[0] = rs ? 0.0f : q.J00;
+          e.A[1] = rs ? 0.0f : q.J01;
+          e.A[2] = rs ? 0.0f : q.J10;
+          e.A[3] = rs ? 0.0f : q.J11;
           e.b[0] = q.c2 - fmaf(q.J00, cp, q.J01 * hp);
           e.b[1] = q.h2 - fmaf(q.J10, cp, q.J11 * hp);
         }
@@ -911,7 +936,7 @@ template <> struct VjpStash<CELL_LINEAR> { float hp; };
 template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
 template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
 
-template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_>
+template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct VjpOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
@@ -987,6 +1012,18 @@ struct VjpOp {
     for (int v = 0; v < V; ++v)
 #pragma unroll
       for (int k = 0; k < S * S; ++k) ln.J0[v][k] = 0.0f;
+    // packed sequences: evaluation e at a sequence's first step starts from the zero state, and its
+    // Jacobian is zero (no adjoint flows back into the previous sequence)
+    uint32_t sb = 0;
+    if constexpr (SEG) sb = seg_bits(a.c.seg, tl.t_lo, T);
+    if constexpr (SEG) {
+#pragma unroll
+      for (int e = 0; e <= L; ++e)
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+#pragma unroll
+          for (int v = 0; v < V; ++v) sp[k][e][v] = ((sb >> e) & 1u) ? 0.0f : sp[k][e][v];
+    }
     // evaluations e = L .. 0; the element of step e takes the (transposed) Jacobian of e + 1
     float Jn[V][S * S];
 #pragma unroll
@@ -1034,8 +1071,9 @@ struct VjpOp {
             for (int k = 0; k < S * S; ++k) ln.J0[v][k] = J[k];
           }
         }
+        const bool live = ok && !(SEG && ((sb >> e) & 1u));
 #pragma unroll
-        for (int k = 0; k < S * S; ++k) Jn[v][k] = ok ? J[k] : 0.0f;
+        for (int k = 0; k < S * S; ++k) Jn[v][k] = live ? J[k] : 0.0f;
       }
     }
   }
@@ -1139,6 +1177,15 @@ __global__ void k_zero(uint4* p, int64_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// packed sequences: offsets cu[0 .. n-1] -> mask bit s for every offset 0 < s < T (the mask was
+// zeroed by k_zero before; offsets outside that range mark nothing)
+__global__ void k_segmask(const int32_t* cu, int64_t n, int64_t T, uint32_t* mask) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int64_t s = cu[j];
+  if (s > 0 && s < T) atomicOr(mask + (s >> 5), 1u << (s & 31));
+}
+
 // fixed-order reduction of the VJP parameter partials:
 //   out[j][d] = sum over rows r = (b, chunk) of partial[chunk][j][b*D + d]
 // A workgroup owns 64 consecutive outputs; its 16 row groups each add every 16th row, then the 16
@@ -1181,7 +1228,7 @@ template <int CELL, int DT, int V, int L>
 __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1, const void* p2,
                                                   const void* p3, const float* w, const float* bias,
                                                   const float* s0, const float* h, int64_t B, int64_t T,
-                                                  int64_t D, uint32_t* out) {
+                                                  int64_t D, const uint32_t* seg, uint32_t* out) {
   constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   const void* pre[4] = {p0, p1, p2, p3};
   const int64_t C = B * D, N = B * T * D;
@@ -1198,9 +1245,13 @@ __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1
       if (t >= T) break;
       const int64_t idx = (b * T + t) * D + d0;
       float prev[S][V], cur[S][V], u[G][V];
+      const bool rs = seg && ((seg[t >> 5] >> (t & 31)) & 1u);   // a packed sequence begins at t
 #pragma unroll
       for (int k = 0; k < S; ++k) {
-        if (t == 0) {
+        if (rs) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) prev[k][v] = 0.0f;
+        } else if (t == 0) {
           if (s0) ldv<V, DT_F32>(s0, (k * B + b) * D + d0, prev[k]);
           else
 #pragma unroll
@@ -1252,11 +1303,18 @@ uint32_t next_tag() {
 int state_size(int cell) { return cell == CELL_LSTM ? 2 : 1; }
 int gate_count(int cell) { return cell == CELL_LSTM ? 4 : (cell == CELL_GRU ? 3 : 2); }
 
-// workspace: [header 4 KiB: tickets, residual slots][look-back words][VJP partials]
+// workspace: [header 4 KiB: tickets, residual slots][packed-sequence mask][look-back words]
+// [VJP partials]; the mask is (T >> 5) + 2 words (read two at a time by seg_bits)
 constexpr size_t kHeader = 4096;
 constexpr size_t kResOffset = 2048;  // residual slots (uint32 float bits) inside the header
 
+// bound on the number of packed sequences (offsets are int32 steps)
+constexpr int64_t kMaxSeqs = INT32_MAX - 1;
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+size_t seg_bytes(int64_t T) { return align256(static_cast<size_t>((T >> 5) + 2) * sizeof(uint32_t)); }
+size_t lb_offset(int64_t T) { return kHeader + seg_bytes(T); }
+uint32_t* seg_mask(void* ws) { return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kHeader); }
 
 struct Geo {
   int V, L, NW, S, nslot;
@@ -1310,7 +1368,8 @@ template <> struct VjpCfg<CELL_LSTM> : TileCfg<PR_VJP_LSTM_CFG> {};
 Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int ticket_slot) {
   Common c;
   char* base = static_cast<char*>(ws);
-  c.lb = reinterpret_cast<uint64_t*>(base + kHeader);
+  c.lb = reinterpret_cast<uint64_t*>(base + lb_offset(T));
+  c.seg = seg_mask(ws);
   c.ticket = reinterpret_cast<uint32_t*>(base) + ticket_slot;
   c.tag = 0;
   c.n_chains = static_cast<int32_t>(g.n_chains);
@@ -1325,6 +1384,16 @@ pararnn_status launch_zero(void* p, size_t bytes, hipStream_t st) {
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n16);
+  return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
+// clear the header, the mask and the look-back words; then mark the packed-sequence starts
+pararnn_status prepare_ws(void* ws, int64_t T, size_t lb_bytes, const int32_t* cu, int64_t n_seqs, hipStream_t st) {
+  pararnn_status rc = launch_zero(ws, lb_offset(T) + align256(lb_bytes), st);
+  if (rc || !cu) return rc;
+  const int64_t n = n_seqs + 1;
+  hipLaunchKernelGGL(k_segmask, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, cu, n, T,
+                     seg_mask(ws));
   return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
 }
 
@@ -1360,24 +1429,26 @@ pararnn_status check_problem(const pararnn_problem* pb) {
   if (pb->cell != CELL_LINEAR && (!pb->w || !pb->bias || !aligned(pb->w, 8) || !aligned(pb->bias, 8)))
     return PARARNN_ERR_INVALID_ARG;
   if (pb->s0 && !aligned(pb->s0, 8)) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cu_seqlens && (!aligned(pb->cu_seqlens, 4) || pb->n_seqs < 0 || pb->n_seqs > kMaxSeqs))
+    return PARARNN_ERR_INVALID_ARG;
   return PARARNN_OK;
 }
 
 int64_t problem_N(const pararnn_problem* pb) { return pb->B * pb->T * pb->D; }
 
 // ---------------- Newton ----------------
-template <int CELL, int DT>
+template <int CELL, int DT, bool SEG>
 struct NewtonKernel {
   using C = NewtonCfg<CELL>;
-  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS>;
+  using Op = NewtonOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS, SEG>;
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
-  static size_t ws(const pararnn_problem* pb) { return kHeader + align256(geo(pb).lb_bytes()); }
+  static size_t ws(const pararnn_problem* pb) { return lb_offset(pb->T) + align256(geo(pb).lb_bytes()); }
   static pararnn_status prepare(const pararnn_problem* pb, void* ws, hipStream_t st) {
     const Geo g = geo(pb);
     if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
-    return launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
+    return prepare_ws(ws, pb->T, g.lb_bytes(), pb->cu_seqlens, pb->n_seqs, st);
   }
   static pararnn_status iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
                                 void* ws, hipStream_t st) {
@@ -1409,7 +1480,7 @@ struct NewtonKernel {
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL((k_residual<CELL, DT, RV, RL>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        pb->pre[0], pb->pre[1], pb->pre[2], pb->pre[3], pb->w, pb->bias, pb->s0, s_out, pb->B,
-                       pb->T, pb->D, res + PARARNN_MAX_ITERS);
+                       pb->T, pb->D, SEG ? seg_mask(ws) : nullptr, res + PARARNN_MAX_ITERS);
     return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
   }
 };
@@ -1421,30 +1492,39 @@ struct NewtonEntry {
   pararnn_status (*final_residual)(const pararnn_problem*, const float*, void*, hipStream_t);
 };
 
-template <int CELL, int DT>
+template <int CELL, int DT, bool SEG>
 NewtonEntry newton_entry() {
-  using K = NewtonKernel<CELL, DT>;
+  using K = NewtonKernel<CELL, DT, SEG>;
   return {K::ws, K::prepare, K::iterate, K::final_residual};
 }
 
-NewtonEntry pick_newton(int cell, int dt) {
-  if (cell == CELL_GRU) return dt == DT_BF16 ? newton_entry<CELL_GRU, DT_BF16>() : newton_entry<CELL_GRU, DT_F32>();
-  if (cell == CELL_LSTM) return dt == DT_BF16 ? newton_entry<CELL_LSTM, DT_BF16>() : newton_entry<CELL_LSTM, DT_F32>();
-  return dt == DT_BF16 ? newton_entry<CELL_LINEAR, DT_BF16>() : newton_entry<CELL_LINEAR, DT_F32>();
+template <int CELL, int DT>
+NewtonEntry newton_entry_seg(bool seg) { return seg ? newton_entry<CELL, DT, true>() : newton_entry<CELL, DT, false>(); }
+
+template <int CELL>
+NewtonEntry newton_entry_dt(int dt, bool seg) {
+  return dt == DT_BF16 ? newton_entry_seg<CELL, DT_BF16>(seg) : newton_entry_seg<CELL, DT_F32>(seg);
+}
+
+NewtonEntry pick_newton(const pararnn_problem* pb) {
+  const bool seg = pb->cu_seqlens != nullptr;
+  if (pb->cell == CELL_GRU) return newton_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
+  if (pb->cell == CELL_LSTM) return newton_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
+  return newton_entry_dt<CELL_LINEAR>(pb->pre_dtype, seg);
 }
 
 // ---------------- linear scan ----------------
-template <int S, int DT, bool REV>
+template <int S, int DT, bool REV, bool SEG>
 struct ScanKernel {
   using C = ScanCfg<S>;
-  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW, C::MINW, C::TS>;
+  using Op = LinearOp<S, DT, REV, C::V, C::L, C::NW, C::MINW, C::TS, SEG>;
   static Geo geo(int64_t B, int64_t T, int64_t D) { return make_geo(S, Op::NSLOT, C::V, C::L, C::NW, C::TS, B, T, D); }
-  static size_t ws(int64_t B, int64_t T, int64_t D) { return kHeader + align256(geo(B, T, D).lb_bytes()); }
+  static size_t ws(int64_t B, int64_t T, int64_t D) { return lb_offset(T) + align256(geo(B, T, D).lb_bytes()); }
   static pararnn_status run(int64_t B, int64_t T, int64_t D, const void* a_, const void* b_, const float* s0,
-                            float* out, void* ws, hipStream_t st) {
+                            const int32_t* cu, int64_t n_seqs, float* out, void* ws, hipStream_t st) {
     const Geo g = geo(B, T, D);
     if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
-    pararnn_status rc = launch_zero(ws, kHeader + align256(g.lb_bytes()), st);
+    pararnn_status rc = prepare_ws(ws, T, g.lb_bytes(), cu, n_seqs, st);
     if (rc) return rc;
     typename Op::Args a;
     a.c = make_common(ws, g, B, T, D, 0);
@@ -1461,25 +1541,31 @@ struct ScanKernel {
 
 struct ScanEntry {
   size_t (*ws)(int64_t, int64_t, int64_t);
-  pararnn_status (*run)(int64_t, int64_t, int64_t, const void*, const void*, const float*, float*, void*, hipStream_t);
+  pararnn_status (*run)(int64_t, int64_t, int64_t, const void*, const void*, const float*, const int32_t*, int64_t,
+                        float*, void*, hipStream_t);
 };
 
+template <int S, int DT, bool REV, bool SEG>
+ScanEntry scan_entry() { return {ScanKernel<S, DT, REV, SEG>::ws, ScanKernel<S, DT, REV, SEG>::run}; }
+
 template <int S, int DT, bool REV>
-ScanEntry scan_entry() { return {ScanKernel<S, DT, REV>::ws, ScanKernel<S, DT, REV>::run}; }
+ScanEntry pick_scan_seg(bool seg) { return seg ? scan_entry<S, DT, REV, true>() : scan_entry<S, DT, REV, false>(); }
 
 template <int S, int DT>
-ScanEntry pick_scan_dir(int rev) { return rev ? scan_entry<S, DT, true>() : scan_entry<S, DT, false>(); }
+ScanEntry pick_scan_dir(int rev, bool seg) {
+  return rev ? pick_scan_seg<S, DT, true>(seg) : pick_scan_seg<S, DT, false>(seg);
+}
 
-ScanEntry pick_scan(int S, int dt, int rev) {
-  if (S == 1) return dt == DT_BF16 ? pick_scan_dir<1, DT_BF16>(rev) : pick_scan_dir<1, DT_F32>(rev);
-  return dt == DT_BF16 ? pick_scan_dir<2, DT_BF16>(rev) : pick_scan_dir<2, DT_F32>(rev);
+ScanEntry pick_scan(int S, int dt, int rev, bool seg) {
+  if (S == 1) return dt == DT_BF16 ? pick_scan_dir<1, DT_BF16>(rev, seg) : pick_scan_dir<1, DT_F32>(rev, seg);
+  return dt == DT_BF16 ? pick_scan_dir<2, DT_BF16>(rev, seg) : pick_scan_dir<2, DT_F32>(rev, seg);
 }
 
 // ---------------- VJP ----------------
-template <int CELL, int DT>
+template <int CELL, int DT, bool SEG>
 struct VjpKernel {
   using C = VjpCfg<CELL>;
-  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS>;
+  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS, SEG>;
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
@@ -1488,14 +1574,14 @@ struct VjpKernel {
   }
   static size_t ws(const pararnn_problem* pb) {
     const Geo g = geo(pb);
-    return kHeader + align256(g.lb_bytes()) + align256(part_bytes(g, pb));
+    return lb_offset(pb->T) + align256(g.lb_bytes()) + align256(part_bytes(g, pb));
   }
   static pararnn_status run(const pararnn_problem* pb, const float* s, const float* gr, float* d_pre, float* d_w,
                             float* d_bias, float* d_s0, float* lam, void* ws, hipStream_t st) {
     const Geo g = geo(pb);
     if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
     const size_t lbb = align256(g.lb_bytes());
-    pararnn_status rc = launch_zero(ws, kHeader + lbb, st);
+    pararnn_status rc = prepare_ws(ws, pb->T, g.lb_bytes(), pb->cu_seqlens, pb->n_seqs, st);
     if (rc) return rc;
     typename Op::Args a;
     a.c = make_common(ws, g, pb->B, pb->T, pb->D, 0);
@@ -1509,7 +1595,7 @@ struct VjpKernel {
     a.d_pre = d_pre;
     a.lambda_out = lam;
     a.d_s0 = d_s0;
-    a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kHeader + lbb);
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + lb_offset(pb->T) + lbb);
     a.B = pb->B;
     a.res_slot = nullptr;
     rc = launch_tile<Op>(a, g, st);
@@ -1533,13 +1619,22 @@ struct VjpEntry {
                         void*, hipStream_t);
 };
 
-template <int CELL, int DT>
-VjpEntry vjp_entry() { return {VjpKernel<CELL, DT>::ws, VjpKernel<CELL, DT>::run}; }
+template <int CELL, int DT, bool SEG>
+VjpEntry vjp_entry() { return {VjpKernel<CELL, DT, SEG>::ws, VjpKernel<CELL, DT, SEG>::run}; }
 
-VjpEntry pick_vjp(int cell, int dt) {
-  if (cell == CELL_GRU) return dt == DT_BF16 ? vjp_entry<CELL_GRU, DT_BF16>() : vjp_entry<CELL_GRU, DT_F32>();
-  if (cell == CELL_LSTM) return dt == DT_BF16 ? vjp_entry<CELL_LSTM, DT_BF16>() : vjp_entry<CELL_LSTM, DT_F32>();
-  return dt == DT_BF16 ? vjp_entry<CELL_LINEAR, DT_BF16>() : vjp_entry<CELL_LINEAR, DT_F32>();
+template <int CELL, int DT>
+VjpEntry vjp_entry_seg(bool seg) { return seg ? vjp_entry<CELL, DT, true>() : vjp_entry<CELL, DT, false>(); }
+
+template <int CELL>
+VjpEntry vjp_entry_dt(int dt, bool seg) {
+  return dt == DT_BF16 ? vjp_entry_seg<CELL, DT_BF16>(seg) : vjp_entry_seg<CELL, DT_F32>(seg);
+}
+
+VjpEntry pick_vjp(const pararnn_problem* pb) {
+  const bool seg = pb->cu_seqlens != nullptr;
+  if (pb->cell == CELL_GRU) return vjp_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
+  if (pb->cell == CELL_LSTM) return vjp_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
+  return vjp_entry_dt<CELL_LINEAR>(pb->pre_dtype, seg);
 }
 
 }  // namespace
@@ -1566,7 +1661,7 @@ const char* pararnn_status_string(int s) {
 size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_newton_opts*) {
   if (check_problem(pb) != PARARNN_OK) return 0;
   if (problem_N(pb) == 0) return kHeader;
-  return pick_newton(pb->cell, pb->pre_dtype).ws(pb);
+  return pick_newton(pb).ws(pb);
 }
 
 namespace {
@@ -1618,7 +1713,7 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
-  if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb->cell, pb->pre_dtype).ws(pb)) return PARARNN_ERR_WORKSPACE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb).ws(pb)) return PARARNN_ERR_WORKSPACE;
   return PARARNN_OK;
 }
 }  // namespace
@@ -1627,7 +1722,7 @@ pararnn_status pararnn_newton_prepare(const pararnn_problem* pb, const pararnn_n
                                       size_t ws_bytes, void* stream) {
   pararnn_status rc = newton_check(pb, op, nullptr, false, ws, ws_bytes);
   if (rc || problem_N(pb) == 0) return rc;
-  return pick_newton(pb->cell, pb->pre_dtype).prepare(pb, ws, static_cast<hipStream_t>(stream));
+  return pick_newton(pb).prepare(pb, ws, static_cast<hipStream_t>(stream));
 }
 
 pararnn_status pararnn_newton_iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
@@ -1635,7 +1730,7 @@ pararnn_status pararnn_newton_iterate(const pararnn_problem* pb, const pararnn_n
   pararnn_status rc = newton_check(pb, op, s_out, true, ws, ws_bytes);
   if (rc || problem_N(pb) == 0) return rc;
   if (k < 0 || k >= budget(pb, op)) return PARARNN_ERR_INVALID_ARG;
-  return pick_newton(pb->cell, pb->pre_dtype).iterate(pb, op, k, s_out, ws, static_cast<hipStream_t>(stream));
+  return pick_newton(pb).iterate(pb, op, k, s_out, ws, static_cast<hipStream_t>(stream));
 }
 
 pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
@@ -1649,7 +1744,7 @@ pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_ne
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (op->final_residual) {
-    rc = pick_newton(pb->cell, pb->pre_dtype).final_residual(pb, s_out, ws, st);
+    rc = pick_newton(pb).final_residual(pb, s_out, ws, st);
     if (rc) return rc;
   }
   if (!report) return PARARNN_OK;
@@ -1687,7 +1782,7 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
   pararnn_status rc = newton_check(pb, op, s_out, true, ws, ws_bytes);
   if (rc) return rc;
   if (problem_N(pb) == 0) return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
-  const NewtonEntry ne = pick_newton(pb->cell, pb->pre_dtype);
+  const NewtonEntry ne = pick_newton(pb);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = ne.prepare(pb, ws, st);
   const int K = budget(pb, op);
@@ -1707,27 +1802,28 @@ int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {
 size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {
   if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return 0;
   if (B * T * D == 0) return kHeader;
-  return pick_scan(S, PARARNN_F32, 0).ws(B, T, D);
+  return pick_scan(S, PARARNN_F32, 0, false).ws(B, T, D);
 }
 
 pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void* a, const void* b,
-                                   const float* s0, float* s_out, int reverse, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   const float* s0, const int32_t* cu_seqlens, int64_t n_seqs, float* s_out,
+                                   int reverse, void* ws, size_t ws_bytes, void* stream) {
   if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return PARARNN_ERR_INVALID_ARG;
   if (dtype != PARARNN_F32 && dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
   if (B > 0 && D > 0 && T > INT64_MAX / (B * D) / 4) return PARARNN_ERR_INVALID_ARG;
   if (B * T * D == 0) return PARARNN_OK;
   if (!a || !b || !s_out) return PARARNN_ERR_INVALID_ARG;
   if (!aligned(a, 4) || !aligned(b, 4) || !aligned(s_out, 4) || (s0 && !aligned(s0, 4))) return PARARNN_ERR_INVALID_ARG;
-  const ScanEntry se = pick_scan(S, dtype, reverse ? 1 : 0);
+  if (cu_seqlens && (!aligned(cu_seqlens, 4) || n_seqs < 0 || n_seqs > kMaxSeqs)) return PARARNN_ERR_INVALID_ARG;
+  const ScanEntry se = pick_scan(S, dtype, reverse ? 1 : 0, cu_seqlens != nullptr);
   if (!ws || !aligned(ws, 256) || ws_bytes < se.ws(B, T, D)) return PARARNN_ERR_WORKSPACE;
-  return se.run(B, T, D, a, b, s0, s_out, ws, static_cast<hipStream_t>(stream));
+  return se.run(B, T, D, a, b, s0, cu_seqlens, n_seqs, s_out, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t pararnn_vjp_workspace_bytes(const pararnn_problem* pb) {
   if (check_problem(pb) != PARARNN_OK) return 0;
   if (problem_N(pb) == 0) return kHeader;
-  return pick_vjp(pb->cell, pb->pre_dtype).ws(pb);
+  return pick_vjp(pb).ws(pb);
 }
 
 pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const float* g, float* d_pre, float* d_w,
@@ -1738,7 +1834,7 @@ pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (!s || !g || !d_pre || !aligned(s, 8) || !aligned(g, 8) || !aligned(d_pre, 8)) return PARARNN_ERR_INVALID_ARG;
   if ((lambda_out && !aligned(lambda_out, 8)) || (d_s0 && !aligned(d_s0, 8))) return PARARNN_ERR_INVALID_ARG;
-  const VjpEntry ve = pick_vjp(pb->cell, pb->pre_dtype);
+  const VjpEntry ve = pick_vjp(pb);
   if (!ws || !aligned(ws, 256) || ws_bytes < ve.ws(pb)) return PARARNN_ERR_WORKSPACE;
   return ve.run(pb, s, g, d_pre, d_w, d_bias, d_s0, lambda_out, ws, static_cast<hipStream_t>(stream));
 }

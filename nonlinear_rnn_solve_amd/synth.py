@@ -155,3 +155,17 @@ def random_state(S: int, B: int, D: int, seed: int, scale: float = 0.5) -> np.nd
     """A random initial state s0 [S][B][D] (for tests of nonzero initial states)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return (rng.standard_normal(size=(S, B, D), dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
+def packed_offsets(T: int, seed: int, mean_len: float, forced=()) -> np.ndarray:
+    """Offsets cu_seqlens (int32, first 0, last T) of sequences packed along T: lengths drawn from a
+    geometric distribution with the given mean (so short and long sequences mix, as in packed
+    training batches), plus the boundaries listed in `forced`.  Empty sequences are kept when two
+    offsets coincide."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cuts = [0]
+    while cuts[-1] < T:
+        cuts.append(cuts[-1] + int(rng.geometric(1.0 / max(mean_len, 1.0))))
+    cuts[-1] = T
+    cuts = sorted(cuts + [int(f) for f in forced if 0 <= int(f) <= T])
+    return np.asarray(cuts, dtype=np.int32)

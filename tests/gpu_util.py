@@ -22,18 +22,18 @@ def dev(x, device="cuda"):
     return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
-def oracle_problem(inp, s0=None, channels=None):
+def oracle_problem(inp, s0=None, channels=None, cu_seqlens=None):
     """Oracle problem over all channels, or over a list of (b, d) channels (as B=1, D=len)."""
     dt = oracle.BF16 if inp.dtype == "bf16" else oracle.F32
     if channels is None:
-        return oracle.Problem(inp.cell, inp.pre, inp.w, inp.bias, s0=s0, dtype=dt)
+        return oracle.Problem(inp.cell, inp.pre, inp.w, inp.bias, s0=s0, dtype=dt, cu_seqlens=cu_seqlens)
     bs = np.array([c[0] for c in channels])
     ds = np.array([c[1] for c in channels])
     pre = [np.ascontiguousarray(p[bs, :, ds].T[None]) for p in inp.pre]   # [1, T, n]
     w = None if inp.w is None else np.ascontiguousarray(inp.w[:, ds])
     bias = None if inp.bias is None else np.ascontiguousarray(inp.bias[:, ds])
     s0s = None if s0 is None else np.ascontiguousarray(s0[:, bs, ds][:, None, :])
-    return oracle.Problem(inp.cell, pre, w, bias, s0=s0s, dtype=dt)
+    return oracle.Problem(inp.cell, pre, w, bias, s0=s0s, dtype=dt, cu_seqlens=cu_seqlens)
 
 
 def take_channels(x, channels):

@@ -40,8 +40,10 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
-                   ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0), sizeof(pararnn_newton_opts),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0),'
+                   ' offsetof(pararnn_problem, cu_seqlens), offsetof(pararnn_problem, n_seqs),'
+                   ' sizeof(pararnn_newton_opts),'
                    ' offsetof(pararnn_newton_opts, final_residual), offsetof(pararnn_newton_opts, init_mode),'
                    ' sizeof(pararnn_report),'
                    ' offsetof(pararnn_report, residual)); return 0;}\n')
@@ -49,6 +51,7 @@ def test_struct_layouts_match_header(tmp_path):
     subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
+            api._Problem.cu_seqlens.offset, api._Problem.n_seqs.offset,
             ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, api._Opts.init_mode.offset,
             ctypes.sizeof(api._Report),
             api._Report.residual.offset]
@@ -98,6 +101,11 @@ def test_validation_codes_without_launching(lib):
     assert solve(_problem(), o=api._Opts(-1, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
+    p = _problem()
+    p.cu_seqlens, p.n_seqs = 4098, 3                          # offsets not 4-byte aligned
+    assert solve(p) == -1
+    p.cu_seqlens, p.n_seqs = 4096, -1
+    assert solve(p) == -1
     assert solve(_problem(), w=ctypes.c_void_p(0)) == -3
     assert solve(_problem(), w=ctypes.c_void_p(4096 + 8)) == -3   # not 256-byte aligned
     assert solve(_problem(), n=16) == -3
@@ -105,13 +113,15 @@ def test_validation_codes_without_launching(lib):
     it = lambda p, k: lib.pararnn_newton_iterate(ctypes.byref(p), ctypes.byref(opts), k, out, ws, 1 << 40, None)  # noqa
     assert it(_problem(), -1) == -1 and it(_problem(), 3) == -1   # k outside [0, max_iters)
     assert lib.pararnn_newton_prepare(ctypes.byref(_problem()), ctypes.byref(opts), ws, 16, None) == -3
-    scan = lambda S, dt, a=4096, n=1 << 40: lib.pararnn_linear_scan(  # noqa: E731
-        S, 8, 100, 64, dt, ctypes.c_void_p(a), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 0,
+    scan = lambda S, dt, a=4096, n=1 << 40, cu=None, ns=0: lib.pararnn_linear_scan(  # noqa: E731
+        S, 8, 100, 64, dt, ctypes.c_void_p(a), ctypes.c_void_p(4096), None, cu, ns, ctypes.c_void_p(4096), 0,
         ctypes.c_void_p(1 << 20), n, None)
     assert scan(3, 0) == -1
     assert scan(1, 9) == -1
     assert scan(1, 0, a=0) == -1
     assert scan(1, 0, n=8) == -3
+    assert scan(1, 0, cu=ctypes.c_void_p(4097), ns=2) == -1
+    assert scan(1, 0, cu=ctypes.c_void_p(4096), ns=-2) == -1
     vjp = lambda p: lib.pararnn_scan_vjp(ctypes.byref(p), None, ctypes.c_void_p(4096),  # noqa: E731
                                          ctypes.c_void_p(4096), None, None, None, None, ws, 1 << 40, None)
     assert vjp(_problem()) == -1                            # trajectory missing
@@ -120,7 +130,7 @@ def test_validation_codes_without_launching(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.pararnn_status_string(s).decode() != "unknown status"
-    assert lib.pararnn_abi_version() == api.ABI_VERSION == 2
+    assert lib.pararnn_abi_version() == api.ABI_VERSION == 3
 
 
 def test_binding_refuses_cpu_tensors():
