@@ -8,6 +8,10 @@ fp32 arithmetic, B=1, T=131072, D=1024): a Newton solve from the zero guess unti
 residual is below 1e-5 (at most 8 iterations), then the reverse-scan VJP for an upstream gradient
 dL/dh ~ N(0, 1).  Other workloads (--workload 0..3) time one Newton solve or one linear scan.
 
+--variants times the same workload with the options built on the method (warm start, the measured
+budget K*(T), packed sequences) and prints one JSON line per variant instead; --kstar times the
+automatic budget over a grid of sequence lengths.  Neither is the benchmark line.
+
 Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
 iterations the solve ran (a linear scan counts K = 1).  roofline: the steady-state fused Newton
 iteration kernel (or the scan kernel), algorithmic bytes per element x elements / its mean
@@ -89,6 +93,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-channels", type=int, default=0, help="channels in the CPU-baseline sample (0: auto)")
+    ap.add_argument("--variants", action="store_true", help="time warm start / K* budget / packed variants")
+    ap.add_argument("--kstar", action="store_true", help="time the automatic budget over a grid of lengths")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many MiB "
                          "(same-box bandwidth context, and the known-size kernel that calibrates HBM counters)")
@@ -109,8 +115,14 @@ def main():
     if args.copy_mib > 0:
         copy_bench(torch, dev, args)
         return
+    if args.kstar:
+        kstar_bench(torch, dev, args)
+        return
     wl = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(wl)
+    if args.variants:
+        variants_bench(torch, dev, args, wl, inp)
+        return
     if wl.dtype == "bf16":
         pre = [torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).to(dev) for p in inp.pre]
     else:
@@ -203,6 +215,99 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, iters, args.cpu_channels)
     print(json.dumps(line), flush=True)
+
+
+def device_inputs(torch, dev, inp):
+    if inp.dtype == "bf16":
+        pre = [torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).to(dev) for p in inp.pre]
+    else:
+        pre = [torch.from_numpy(p).to(dev) for p in inp.pre]
+    w = torch.from_numpy(inp.w).to(dev) if inp.w is not None else None
+    b = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    g = torch.from_numpy(inp.g).to(dev) if inp.g is not None else None
+    return pre, w, b, g
+
+
+def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **opts):
+    """Mean wall time of one solve (+ VJP), its iteration count, and the mean duration of the
+    steady-state iteration kernels that did work (HIP events on the launch stream)."""
+    stream = torch.cuda.current_stream(out.device)
+    recs = []
+
+    def one(record):
+        rec = []
+
+        def hook(k, phase):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            if phase == "before":
+                rec.append([k, ev, None])
+            else:
+                rec[-1][2] = ev
+        _, rep_ = api.newton_solve(cell, pre, w, b, out=out, on_iteration=hook, **opts)
+        if vjp:
+            api.scan_vjp(cell, pre, out, g, w, b, want_s0=False, cu_seqlens=opts.get("cu_seqlens"))
+        if record:
+            recs.append(rec)
+        return rep_.iters
+    for _ in range(warmup):
+        one(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        iters = one(True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # steady-state iterations (k >= 1) when there are any: iteration 0 of a zero start reads no iterate
+    durs = [e0.elapsed_time(e1) for rec in recs for k, e0, e1 in rec if (1 if iters > 1 else 0) <= k < iters]
+    return ms, iters, float(np.mean(durs))
+
+
+def variants_bench(torch, dev, args, wl, inp):
+    """The workload's solve (and VJP) with each option the method adds, one JSON line each."""
+    from nonlinear_rnn_solve_amd import api, synth
+    pre, w, b, g = device_inputs(torch, dev, inp)
+    N = wl.B * wl.T * wl.D
+    out = torch.empty((inp.S, wl.B, wl.T, wl.D), dtype=torch.float32, device=dev)
+    cu = synth.packed_offsets(wl.T, 2700, 2048)
+    tcu = torch.from_numpy(cu).to(dev)
+    tol = wl.tol if wl.tol > 0 else 0.0
+    base = dict(max_iters=wl.max_iters, tol=tol)
+    variants = [
+        ("zero start (benchmark line)", base),
+        ("warm start", dict(base, warm_start=True)),
+        ("measured budget K*(T), zero start", dict(max_iters=None)),
+        ("measured budget K*(T), warm start", dict(max_iters=None, warm_start=True)),
+        ("packed sequences, mean length 2048 (%d sequences)" % (len(cu) - 1), dict(base, cu_seqlens=tcu)),
+    ]
+    for name, opts in variants:
+        ms, iters, kern = time_solve(torch, api, wl.cell, pre, w, b, g, out, args.steps, args.warmup,
+                                     vjp=wl.vjp, **opts)
+        per_elem = algo_bytes(wl.cell, wl.dtype)
+        print(json.dumps({"workload": wl.name, "variant": name, "ms_per_solve": ms, "iters": iters,
+                          "channel_tokens_per_s": N * iters / (ms * 1e-3), "vjp": wl.vjp,
+                          "iteration_kernel_ms": kern,
+                          "iteration_gbs": per_elem * N / (kern * 1e-3) / 1e9}), flush=True)
+
+
+def kstar_bench(torch, dev, args):
+    """Wall time of a solve at the measured budget K*(T), zero and warm start, on the grid of lengths
+    the budget was measured on (B = 1, D = 1024; GRU bf16 gate inputs, LSTM fp32)."""
+    from nonlinear_rnn_solve_amd import api, synth
+    for cell, dtype in (("gru", "bf16"), ("lstm", "f32")):
+        for T in (1024, 4096, 16384, 65536, 131072):
+            inp = synth.make_inputs(cell, 1, T, 1024, dtype=dtype, seed=3000 + T // 1024 + (500 if cell == "lstm" else 0))
+            pre, w, b, _ = device_inputs(torch, dev, inp)
+            out = torch.empty((inp.S, 1, T, 1024), dtype=torch.float32, device=dev)
+            for warm in (False, True):
+                ms, iters, kern = time_solve(torch, api, cell, pre, w, b, None, out, args.steps, args.warmup,
+                                             max_iters=None, warm_start=warm)
+                print(json.dumps({"cell": cell, "storage": dtype, "B": 1, "T": T, "D": 1024,
+                                  "init": "warm" if warm else "zero", "kstar": iters, "ms_per_solve": ms,
+                                  "iteration_kernel_ms": kern,
+                                  "channel_tokens_per_s": T * 1024 * iters / (ms * 1e-3)}), flush=True)
+            del pre, out
+            torch.cuda.empty_cache()
 
 
 def copy_bench(torch, dev, args):
