@@ -133,6 +133,58 @@ DEV void stv(float* p, const float (&x)[V]) {
   }
 }
 
+// the same loads and stores addressed as a uniform base element plus the lane's 32-bit offset, so
+// that each one is a scalar base register and one vector offset (no per-load 64-bit vector adds)
+template <int V, int DT>
+DEV void ldv_u(const void* plane, int64_t ubase, uint32_t loff, float (&o)[V]) {
+  constexpr int ESZ = DT == DT_F32 ? 4 : 2;
+  const char* p = static_cast<const char*>(plane) + ubase * ESZ + static_cast<uint64_t>(loff * ESZ);
+  ldv<V, DT>(p, 0, o);
+}
+// raw buffer view of one plane from a uniform base address: a load is (descriptor, 32-bit lane
+// byte offset, 32-bit uniform byte offset) with no vector address arithmetic at all.  Word 3 is
+// the raw-buffer format of the gfx9 family; the 4 GiB record count disables range checking
+// within the window (callers keep every offset inside the plane).
+#ifndef PR_FAST_S2
+#define PR_FAST_S2 1
+#endif
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+DEV Rsrc rsrc_at(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), -1, 0x00020000);
+}
+template <int V, int DT>
+DEV void ldv_buf(Rsrc r, uint32_t voff, uint32_t soff, float (&o)[V]) {
+  if constexpr (DT == DT_F32) {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    } else if constexpr (V == 2) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+      o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
+    } else {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+      o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
+      o[2] = __uint_as_float(t[2]); o[3] = __uint_as_float(t[3]);
+    }
+  } else {
+    if constexpr (V == 1) {
+      o[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+    } else if constexpr (V == 2) {
+      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+      o[0] = __uint_as_float(t << 16); o[1] = __uint_as_float(t & 0xffff0000u);
+    } else {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+      o[0] = __uint_as_float(t[0] << 16); o[1] = __uint_as_float(t[0] & 0xffff0000u);
+      o[2] = __uint_as_float(t[1] << 16); o[3] = __uint_as_float(t[1] & 0xffff0000u);
+    }
+  }
+}
+
+template <int V>
+DEV void stv_u(float* plane, int64_t ubase, uint32_t loff, const float (&x)[V]) {
+  char* p = reinterpret_cast<char*>(plane + ubase) + static_cast<uint64_t>(loff * 4u);
+  stv<V>(reinterpret_cast<float*>(p), x);
+}
+
 // ------------------------------------------------------------------------------------------------
 // affine maps x -> A x + b on the S-dimensional state (Blelloch's first-order-recurrence
 // operator).  compose(later, earlier) = later o earlier; associative, not commutative.
@@ -219,6 +271,8 @@ struct Common {
   int32_t n_chains;     // channel tiles
   int64_t n_chunks;     // time chunks
   int64_t T, D, C, N;   // time steps, channels per row, B*D channels, B*T*D elements
+  int32_t off32;        // every lane's offset from its wave's base element fits 32 bits (in bytes
+                        // of fp32): full tiles address memory as uniform base + 32-bit offset
 };
 
 // Packed sequences: 32 mask bits starting at step t0 (bit i <-> step t0 + i).  The mask has
@@ -236,6 +290,8 @@ DEV uint32_t seg_bits(const uint32_t* seg, int64_t t0, int64_t T) {
 // segments of L steps are stacked in time: wave w, slice s -> segment w*TS + s.
 struct Tile {
   int64_t p, chunk, t_lo, ch0, b, d0;
+  int64_t wbase;     // uniform over the wave: element (row, step, channel) of the wave's first lane
+  uint32_t loff;     // this lane's element offset from wbase (valid when Common::off32)
   int chain, wave, lane, slice, qlane;
   int nvalid;        // steps of this lane inside [0, T); the same for every lane of a slice
   bool active;       // the lane's channels exist
@@ -256,9 +312,83 @@ DEV uint64_t* word_at(const Common& c, int64_t p, int chain, int slot, int q) {
 // positions p-1, p-2, ... are read in windows of W; an inclusive word (the state at the end of
 // that chunk) ends the walk, an aggregate word (the chunk's affine map) extends it.  Position 0
 // publishes its inclusive word without waiting, so the walk always ends.
+#ifndef PR_LB_JOINT
+#define PR_LB_JOINT 1
+#endif
+#ifndef PR_LB_W1
+#define PR_LB_W1 2   // look-back window (predecessors per round) for state size 1
+#endif
 template <int S, int V, int TW, int NSLOT, int W>
 DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
+#if PR_LB_JOINT
+  // all V channels of the lane walk together: one predecessor's words for every channel are loaded
+  // in the same round (its publishing lane wrote them together), so V channels cost one walk
+  Aff<S> acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = aff_id<S>();
+  int64_t m = tl.p - 1;
+  bool done = false;
+  while (!done) {
+    uint64_t wi[W][V][S], wa[W][V][NA];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int64_t mm = m - j;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int q = tl.qlane * V + v;
+        if (mm >= 0) {
+#pragma unroll
+          for (int k = 0; k < S; ++k) wi[j][v][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, k, q));
+#pragma unroll
+          for (int k = 0; k < NA; ++k) wa[j][v][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, S + k, q));
+        } else {
+#pragma unroll
+          for (int k = 0; k < S; ++k) wi[j][v][k] = 0;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) wa[j][v][k] = 0;
+        }
+      }
+    }
+    bool stalled = false;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      if (done || stalled) continue;
+      bool inc_ok = true, agg_ok = true;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[j][v][k], c.tag);
+#pragma unroll
+        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[j][v][k], c.tag);
+      }
+      if (inc_ok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float x[S];
+#pragma unroll
+          for (int k = 0; k < S; ++k) x[k] = word_val(wi[j][v][k]);
+          apply(acc[v], x);
+#pragma unroll
+          for (int k = 0; k < S; ++k) carry[v][k] = x[k];
+        }
+        done = true;
+      } else if (agg_ok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          Aff<S> e;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[j][v][k]));
+          acc[v] = compose(acc[v], e);
+        }
+        --m;
+      } else {
+        stalled = true;
+      }
+    }
+    if (!done && stalled) __builtin_amdgcn_s_sleep(1);
+  }
+#else
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int q = tl.qlane * V + v;
@@ -312,6 +442,7 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
       if (!done && stalled) __builtin_amdgcn_s_sleep(1);
     }
   }
+#endif
 }
 
 DEV float wave_nanmax(float m) {
@@ -362,8 +493,32 @@ void k_tile(const typename Op::Args a) {
   tl.t_lo = tl.chunk * static_cast<int64_t>(NW * TS * L) + (tl.wave * TS + tl.slice) * L;
   tl.ch0 = static_cast<int64_t>(tl.chain) * TW + tl.qlane * V;
   tl.active = tl.ch0 < c.C;
-  tl.b = tl.active ? tl.ch0 / c.D : 0;
-  tl.d0 = tl.active ? tl.ch0 - tl.b * c.D : 0;
+  {
+    // row b and channel d0 of ch0: the tile's first channel is uniform, so its division is scalar;
+    // a lane is less than TW channels further, which wraps into the next row at most once when
+    // D >= TW (otherwise a small 32-bit division)
+    const int64_t tc0 = static_cast<int64_t>(tl.chain) * TW;
+    const int64_t b0 = tc0 / c.D;
+    int64_t d = tc0 - b0 * c.D + tl.qlane * V, b = b0;
+    if (c.D >= TW) {
+      if (d >= c.D) { d -= c.D; ++b; }
+    } else {
+      const uint32_t q = static_cast<uint32_t>(d) / static_cast<uint32_t>(c.D);
+      b += q;
+      d -= static_cast<int64_t>(q) * c.D;
+    }
+    tl.b = tl.active ? b : 0;
+    tl.d0 = tl.active ? d : 0;
+    // uniform base of the wave (its first slice, the tile's first channel) and the lane's offset;
+    // lanes past the last channel read the tile's first channel, like the 64-bit path
+    const int wave_u = __builtin_amdgcn_readfirstlane(tl.wave);
+    const int64_t t_w = tl.chunk * static_cast<int64_t>(NW * TS * L) + static_cast<int64_t>(wave_u) * TS * L;
+    const int64_t d_w = tc0 - b0 * c.D;
+    tl.wbase = (b0 * c.T + t_w) * c.D + d_w;
+    const int64_t lo = tl.active ? (tl.b - b0) * c.T * c.D + static_cast<int64_t>(tl.slice) * L * c.D + (tl.d0 - d_w)
+                                 : static_cast<int64_t>(tl.slice) * L * c.D;
+    tl.loff = static_cast<uint32_t>(lo);
+  }
   tl.first_seg = tl.wave == 0 && tl.slice == 0;
   tl.last_seg = tl.wave == NW - 1 && tl.slice == TS - 1;
   {
@@ -625,7 +780,7 @@ struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = REV, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
   struct Args {
     Common c;
     const void* a;
@@ -714,7 +869,7 @@ struct NewtonOp {
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
-  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
   struct Args {
     Common c;
     const void* pre[4];
@@ -770,7 +925,19 @@ struct NewtonOp {
     // step before the lane's first) and the gate inputs of the lane's L steps
     float h[S][L + 1][V];
     float u[G][L][V];
-    if (have_h) {
+    const bool fast = !MASKED && c.off32 && (S == 1 || PR_FAST_S2);   // uniform
+    if (have_h && fast) {
+      // one descriptor per state plane at the wave's step before its first; step i is i+1 rows on
+      // (the base may lie before the plane when the wave starts at t = 0: that halo is not loaded)
+      const uint32_t vo = tl.loff * 4u, row_b = static_cast<uint32_t>(D) * 4u;
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const Rsrc r = rsrc_at(a.h_in + (k * N + tl.wbase - D));
+#pragma unroll
+        for (int i = 0; i < L; ++i) ldv_buf<V, DT_F32>(r, vo, (i + 1) * row_b, h[k][i + 1]);
+        if (!tl.first_seg) ldv_buf<V, DT_F32>(r, vo, 0u, h[k][0]);
+      }
+    } else if (have_h) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
         const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
@@ -791,11 +958,22 @@ struct NewtonOp {
 #pragma unroll
           for (int v = 0; v < V; ++v) h[k][i][v] = 0.0f;
     }
+    if (fast) {
+      constexpr uint32_t ESZ = DT == DT_F32 ? 4u : 2u;
+      const uint32_t vo = tl.loff * ESZ, row_b = static_cast<uint32_t>(D) * ESZ;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
+      for (int g = 0; g < G; ++g) {
+        const Rsrc r = rsrc_at(static_cast<const char*>(a.pre[g]) + tl.wbase * ESZ);
 #pragma unroll
-      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], (row + t) * D + tl.d0, u[g][i]);
+        for (int i = 0; i < L; ++i) ldv_buf<V, DT>(r, vo, i * row_b, u[g][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const int64_t t = MASKED ? clamp_t(tl.t_lo + i, T) : tl.t_lo + i;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], (row + t) * D + tl.d0, u[g][i]);
+      }
     }
     Params<G, V> pm;
     if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(a.w, a.bias, D, tl.d0, pm);
@@ -910,6 +1088,7 @@ struct NewtonOp {
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
     if (!tl.active) return;
     const int64_t base = (tl.b * a.c.T + tl.t_lo) * a.c.D + tl.d0;
+    const bool fast = a.c.off32 && tl.nvalid == L;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       if (i >= tl.nvalid) continue;
@@ -920,7 +1099,8 @@ struct NewtonOp {
         float o[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) o[v] = x[v][k];
-        stv<V>(a.h_out + k * a.c.N + base + i * a.c.D, o);
+        if (fast) stv_u<V>(a.h_out, k * a.c.N + tl.wbase + i * a.c.D, tl.loff, o);
+        else stv<V>(a.h_out + k * a.c.N + base + i * a.c.D, o);
       }
     }
   }
@@ -942,7 +1122,7 @@ struct VjpOp {
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = true, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? 4 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
   static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
   struct Args {
     Common c;
@@ -1375,6 +1555,11 @@ Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int 
   c.n_chains = static_cast<int32_t>(g.n_chains);
   c.n_chunks = g.n_chunks;
   c.T = T; c.D = D; c.C = B * D; c.N = B * T * D;
+  // largest lane offset from its wave's base element: a lane is at most ceil(TW / D) rows further
+  // (the row length T*D each), TS*L steps, and less than TW + D channels away; in fp32 bytes
+  const int64_t rows = (g.TW + D - 1) / D;
+  const double max_off = (static_cast<double>(rows) * T * D + static_cast<double>(g.CT) * D + g.TW + D) * 4.0;
+  c.off32 = max_off < 4294967296.0 ? 1 : 0;
   return c;
 }
 
