@@ -25,8 +25,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-GATES = {"linear": 2, "gru": 3, "lstm": 4}
-STATE = {"linear": 1, "gru": 1, "lstm": 2}
+GATES = {"linear": 2, "gru": 3, "lstm": 4, "slstm": 4}
+STATE = {"linear": 1, "gru": 1, "lstm": 2, "slstm": 4}
 
 
 @dataclass(frozen=True)
@@ -118,7 +118,8 @@ def make_inputs(cell: str, B: int, T: int, D: int, dtype: str = "f32", seed: int
 
     Draw order: pre-activation planes in gate order, then recurrent weights
     [G][D], then biases [G][D], then (if asked) the upstream gradient.
-    Gate orders: gru (z, r, c); lstm (i, f, o, g); linear (a, b).
+    Gate orders: gru (z, r, c); lstm (i, f, o, g); slstm (z, i, f, o); linear (a, b).
+    Biases ~ N(0, 0.1^2), except the forget gate's (lstm, slstm), which is 1.
     """
     assert cell in GATES and dtype in ("f32", "bf16")
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -134,6 +135,11 @@ def make_inputs(cell: str, B: int, T: int, D: int, dtype: str = "f32", seed: int
         w = _uniform_half(rng, (G, D))
         if cell == "gru":
             bias = (rng.standard_normal(size=(G, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+        elif cell == "slstm":
+            drawn = (rng.standard_normal(size=(3, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+            bias = np.empty((4, D), dtype=np.float32)
+            bias[0], bias[1], bias[3] = drawn[0], drawn[1], drawn[2]   # z, i, o
+            bias[2] = 1.0                                               # forget gate
         else:
             drawn = (rng.standard_normal(size=(3, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
             bias = np.empty((4, D), dtype=np.float32)

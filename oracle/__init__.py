@@ -1,7 +1,7 @@
 """CPU oracle for the ParaRNN hot path -- TEST INFRASTRUCTURE ONLY.
 
 A plain fp64 implementation (``pararnn_oracle.c``) of what the GPU library
-computes: the sequential unroll of a diagonal GRU / LSTM / linear cell, Newton
+computes: the sequential unroll of a diagonal GRU / LSTM / sLSTM / linear cell, Newton
 on F(H)_t = h_t - f(h_{t-1}, x_t) = 0 with a *sequential* linear solve, the
 linear recurrence itself (forward and reverse, state size 1 or 2), and the
 adjoint (VJP) at a solved trajectory.  Sources: pararnn-torch README (PyPI
@@ -27,18 +27,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pararnn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-LINEAR, GRU, LSTM = 0, 1, 2
+LINEAR, GRU, LSTM, SLSTM = 0, 1, 2, 3
 F32, BF16 = 0, 1
-CELLS = {"linear": LINEAR, "gru": GRU, "lstm": LSTM}
+CELLS = {"linear": LINEAR, "gru": GRU, "lstm": LSTM, "slstm": SLSTM}
 OK, EINVAL, ENOMEM, DIVERGED = 0, -1, -2, -5
 
 
 def state_size(cell: int) -> int:
-    return 2 if cell == LSTM else 1
+    return {LINEAR: 1, GRU: 1, LSTM: 2, SLSTM: 4}[cell]
 
 
 def gate_count(cell: int) -> int:
-    return {LINEAR: 2, GRU: 3, LSTM: 4}[cell]
+    return {LINEAR: 2, GRU: 3, LSTM: 4, SLSTM: 4}[cell]
 
 
 def build(force: bool = False) -> str:
@@ -63,10 +63,10 @@ def _load():
         lib.or_cell_step.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.or_unroll.argtypes = [vp, vp, i32]
         lib.or_residual.argtypes = [vp, vp, vp, i32]
-        lib.or_newton.argtypes = [vp, vp, i32, i32, dbl, vp, vp, vp, vp, i32]
+        lib.or_newton.argtypes = [vp, vp, i32, i32, i32, dbl, vp, vp, vp, vp, i32]
         lib.or_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, i32]
         lib.or_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        assert lib.or_abi_version() == 5
+        assert lib.or_abi_version() == 6
         _lib = lib
     return _lib
 
@@ -172,15 +172,17 @@ def residual(prob: Problem, H, nthreads=None) -> float:
     return float(m[0])
 
 
-def newton(prob: Problem, max_iters, tol=0.0, init_guess=None, nthreads=None, warm=False):
+def newton(prob: Problem, max_iters, tol=0.0, init_guess=None, nthreads=None, warm=False, picard=0):
     """Newton with sequential linear solves. Returns (H fp64, residuals[iters], iters, converged, status).
 
-    warm=True starts from H^0_t = f(0, x_t) (ignored when init_guess is given)."""
+    warm=True starts from H^0_t = f(0, x_t) (ignored when init_guess is given); the first `picard`
+    of the max_iters updates are Picard sweeps H^{k+1}_t = f(H^k_{t-1}, x_t)."""
     H = np.zeros(prob.traj_shape(), dtype=np.float64)
     res = np.zeros(max(1, max_iters))
     it, conv = ctypes.c_int(0), ctypes.c_int(0)
     ig = None if init_guess is None else np.ascontiguousarray(init_guess, dtype=np.float32).reshape(prob.traj_shape())
-    rc = _check(_load().or_newton(ctypes.byref(prob.struct), _ptr(ig), 1 if warm else 0, int(max_iters), float(tol), _ptr(H),
+    rc = _check(_load().or_newton(ctypes.byref(prob.struct), _ptr(ig), 1 if warm else 0, int(picard), int(max_iters),
+                                  float(tol), _ptr(H),
                                   _ptr(res), ctypes.byref(it), ctypes.byref(conv), nthreads or default_threads()),
                 "newton")
     return H, res[: it.value].copy(), it.value, bool(conv.value), rc

@@ -34,7 +34,9 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1 };
-enum { OR_LINEAR = 0, OR_GRU = 1, OR_LSTM = 2 };
+enum { OR_LINEAR = 0, OR_GRU = 1, OR_LSTM = 2, OR_SLSTM = 3 };
+/* largest state size and gate count of the cells below */
+enum { OR_SMAX = 4, OR_GMAX = 4 };
 enum { OR_OK = 0, OR_EINVAL = -1, OR_ENOMEM = -2, OR_DIVERGED = -5 };
 
 /* ------------------------------------------------------------------------ */
@@ -56,10 +58,13 @@ static double load_in(const void* p, int dtype, int64_t i) {
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-static int state_size(int cell) { return cell == OR_LSTM ? 2 : 1; }
+static int state_size(int cell) { return cell == OR_SLSTM ? 4 : (cell == OR_LSTM ? 2 : 1); }
 static int gate_count(int cell) {
-  return cell == OR_LSTM ? 4 : (cell == OR_GRU ? 3 : 2);
+  return (cell == OR_LSTM || cell == OR_SLSTM) ? 4 : (cell == OR_GRU ? 3 : 2);
 }
+
+/* log(sigmoid(x)) without overflow for either sign of x */
+static double log_sigmoid(double x) { return x >= 0.0 ? -log1p(exp(-x)) : x - log1p(exp(x)); }
 
 /* ------------------------------------------------------------------------ */
 /* one cell step                                                            */
@@ -79,6 +84,15 @@ static int gate_count(int cell) {
  * LSTM (state (c, h); gates i, f, o, g; textbook cell, diagonal w on h):
  *   i,f,o = sig(U + w h + b),  g = tanh(U_g + w_g h + b_g)
  *   c' = f c + i g,  h' = o tanh(c')
+ * sLSTM, diagonal recurrence (state (c, n, m, h); gates z, i, f, o): the
+ * published sLSTM (xLSTM, Beck et al. 2024) with exponential input gate,
+ * sigmoid forget gate and its log-domain stabiliser m (a reading: the pages
+ * name the cell, ParaSLSTM with mix="diag", but print no equations):
+ *   u_g = U_g + w_g h + b_g,  z = tanh(u_z),  o = sig(u_o),  lf = log sig(u_f)
+ *   m' = max(lf + m, u_i),  i' = exp(u_i - m'),  f' = exp(lf + m - m')
+ *   c' = f' c + i' z,  n' = f' n + i',  h' = o c' / n'
+ * At a tie of the max the forget branch is taken; its derivative is the
+ * branch's (the max is piecewise linear).
  * LINEAR (state h; "gates" a, b are the coefficients themselves):
  *   h' = a h + b
  * u[] for LINEAR holds (a_t, b_t); w and bias are ignored.
@@ -146,6 +160,51 @@ int or_cell_step(int cell, const double* u_in, const double* w,
       J[1] = dc_dh;     /* d c'/d h */
       J[2] = kh * fg;   /* d h'/d c */
       J[3] = dh_dh;     /* d h'/d h */
+    }
+    return OR_OK;
+  }
+  if (cell == OR_SLSTM) {
+    double c = s[0], n = s[1], m = s[2], h = s[3];
+    double uz = u_in[0] + w[0] * h + bias[0], ui = u_in[1] + w[1] * h + bias[1];
+    double uf = u_in[2] + w[2] * h + bias[2], uo = u_in[3] + w[3] * h + bias[3];
+    double z = tanh(uz), o = sigmoid(uo);
+    double lf = log_sigmoid(uf), dlf = sigmoid(-uf); /* d lf / d u_f */
+    int fb = lf + m >= ui;                           /* the forget term sets m' */
+    double m2 = fb ? lf + m : ui;
+    double ip = exp(ui - m2), fp = exp(lf + m - m2);
+    double c2 = fp * c + ip * z, n2 = fp * n + ip, h2 = o * c2 / n2;
+    s_next[0] = c2; s_next[1] = n2; s_next[2] = m2; s_next[3] = h2;
+    /* m', i', f' as functions of (u_i, u_f, m) */
+    double dm_ui = fb ? 0.0 : 1.0, dm_uf = fb ? dlf : 0.0, dm_m = fb ? 1.0 : 0.0;
+    double dip_ui = ip * (1.0 - dm_ui), dip_uf = -ip * dm_uf, dip_m = -ip * dm_m;
+    double dfp_ui = -fp * dm_ui, dfp_uf = fp * (dlf - dm_uf), dfp_m = fp * (1.0 - dm_m);
+    /* d (c', n', m') / d u_g, gate order z, i, f, o */
+    double dc_du[4] = {ip * (1.0 - z * z), c * dfp_ui + z * dip_ui, c * dfp_uf + z * dip_uf, 0.0};
+    double dn_du[4] = {0.0, n * dfp_ui + dip_ui, n * dfp_uf + dip_uf, 0.0};
+    double dm_du[4] = {0.0, dm_ui, dm_uf, 0.0};
+    double dh_du[4];
+    for (int g = 0; g < 4; ++g) dh_du[g] = o * (dc_du[g] * n2 - c2 * dn_du[g]) / (n2 * n2);
+    dh_du[3] += (c2 / n2) * o * (1.0 - o);
+    if (dfdu) {
+      for (int g = 0; g < 4; ++g) {
+        dfdu[0 * 4 + g] = dc_du[g]; dfdu[1 * 4 + g] = dn_du[g];
+        dfdu[2 * 4 + g] = dm_du[g]; dfdu[3 * 4 + g] = dh_du[g];
+      }
+    }
+    if (wcoef) { for (int g = 0; g < 4; ++g) wcoef[g] = h; }
+    if (J) {
+      double dc_m = c * dfp_m + z * dip_m, dn_m = n * dfp_m + dip_m;
+      double sc = 0.0, sn_ = 0.0, sm = 0.0, sh = 0.0; /* h enters every gate through w_g h */
+      for (int g = 0; g < 4; ++g) {
+        sc += dc_du[g] * w[g]; sn_ += dn_du[g] * w[g]; sm += dm_du[g] * w[g]; sh += dh_du[g] * w[g];
+      }
+      J[0] = fp;  J[1] = 0.0; J[2] = dc_m;  J[3] = sc;
+      J[4] = 0.0; J[5] = fp;  J[6] = dn_m;  J[7] = sn_;
+      J[8] = 0.0; J[9] = 0.0; J[10] = dm_m; J[11] = sm;
+      J[12] = o * fp / n2;                          /* d h' / d c */
+      J[13] = -o * c2 * fp / (n2 * n2);             /* d h' / d n */
+      J[14] = o * (dc_m * n2 - c2 * dn_m) / (n2 * n2);
+      J[15] = sh;
     }
     return OR_OK;
   }
@@ -254,7 +313,7 @@ static int run_channels(int64_t n_channels, int nthreads, channel_fn fn, void* c
 
 static int check_problem(const or_problem* p) {
   if (!p || p->B < 0 || p->T < 0 || p->D < 0) return OR_EINVAL;
-  if (p->cell != OR_LINEAR && p->cell != OR_GRU && p->cell != OR_LSTM) return OR_EINVAL;
+  if (p->cell != OR_LINEAR && p->cell != OR_GRU && p->cell != OR_LSTM && p->cell != OR_SLSTM) return OR_EINVAL;
   if (p->dtype != OR_F32 && p->dtype != OR_BF16) return OR_EINVAL;
   int G = gate_count(p->cell);
   for (int g = 0; g < G; ++g)
@@ -277,7 +336,7 @@ static void unroll_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   unroll_ctx* c = (unroll_ctx*)vctx;
   const or_problem* p = c->p;
   int S = state_size(p->cell);
-  double u[4], w[4], bias[4], s[2], sn[2];
+  double u[OR_GMAX], w[OR_GMAX], bias[OR_GMAX], s[OR_SMAX], sn[OR_SMAX];
   for (int64_t ch = ch0; ch < ch1; ++ch) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
@@ -318,7 +377,7 @@ static void resid_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   resid_ctx* c = (resid_ctx*)vctx;
   const or_problem* p = c->p;
   int S = state_size(p->cell);
-  double u[4], w[4], bias[4], prev[2], sn[2], m = 0.0;
+  double u[OR_GMAX], w[OR_GMAX], bias[OR_GMAX], prev[OR_SMAX], sn[OR_SMAX], m = 0.0;
   for (int64_t ch = ch0; ch < ch1; ++ch) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
@@ -372,6 +431,7 @@ typedef struct {
   double* H;          /* in/out trajectory [S][B][T][D] */
   double* worker_max;
   double* scratch;    /* per worker: T * (S + S*S + S) doubles */
+  int picard;         /* this update is a Picard sweep: J taken as 0, so H^{k+1}_t = f(H^k_{t-1}) */
 } newton_ctx;
 
 static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
@@ -382,7 +442,7 @@ static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   double* r = c->scratch + (size_t)worker * (size_t)T * (size_t)(2 * S + S * S);
   double* J = r + T * S;
   double* delta = J + T * S * S;
-  double u[4], w[4], bias[4], prev[2], sn[2], m = 0.0;
+  double u[OR_GMAX], w[OR_GMAX], bias[OR_GMAX], prev[OR_SMAX], sn[OR_SMAX], m = 0.0;
   for (int64_t ch = ch0; ch < ch1; ++ch) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
@@ -391,8 +451,9 @@ static void newton_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
       prev_state(p, c->H, b, t, d, prev);
       gather_u(p, b, t, d, u);
       or_cell_step(p->cell, u, w, bias, prev, sn, J + t * S * S, NULL, NULL);
-      /* where a sequence begins, h_{t-1} does not enter f: that step's Jacobian is zero */
-      if (starts_at(p, t)) for (int k = 0; k < S * S; ++k) J[t * S * S + k] = 0.0;
+      /* where a sequence begins, h_{t-1} does not enter f: that step's Jacobian is zero; a
+         Picard sweep drops the Jacobian everywhere */
+      if (c->picard || starts_at(p, t)) for (int k = 0; k < S * S; ++k) J[t * S * S + k] = 0.0;
       for (int k = 0; k < S; ++k) {
         r[t * S + k] = c->H[traj_index(p, k, b, t, d)] - sn[k];
         m = nan_max(m, fabs(r[t * S + k]));
@@ -425,7 +486,7 @@ static void warm_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   warm_ctx* c = (warm_ctx*)vctx;
   const or_problem* p = c->p;
   int S = state_size(p->cell);
-  double u[4], w[4], bias[4], zero[2] = {0.0, 0.0}, sn[2];
+  double u[OR_GMAX], w[OR_GMAX], bias[OR_GMAX], zero[OR_SMAX] = {0.0, 0.0, 0.0, 0.0}, sn[OR_SMAX];
   for (int64_t ch = ch0; ch < ch1; ++ch) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
@@ -437,9 +498,12 @@ static void warm_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   }
 }
 
-/* init_mode: 0 = init_guess or zeros, 1 = warm start (ignored when init_guess is given) */
-int or_newton(const or_problem* p, const float* init_guess, int init_mode, int max_iters, double tol,
-              double* H, double* resid, int* iters, int* converged, int nthreads) {
+/* init_mode: 0 = init_guess or zeros, 1 = warm start (ignored when init_guess is given).
+   picard_iters: the first min(picard_iters, max_iters) updates are Picard (fixed-point) sweeps
+   H^{k+1}_t = f(H^k_{t-1}, x_t) instead of Newton updates (pararnn-torch README, "API overview":
+   Picard iterations warm the first guess for the sLSTM); they count as iterations. */
+int or_newton(const or_problem* p, const float* init_guess, int init_mode, int picard_iters, int max_iters,
+              double tol, double* H, double* resid, int* iters, int* converged, int nthreads) {
   int rc = check_problem(p);
   if (rc) return rc;
   if (max_iters < 1) return OR_EINVAL;
@@ -456,9 +520,10 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int m
   double* scratch = (double*)malloc(sizeof(double) * (size_t)nthreads *
                                     (size_t)(p->T > 0 ? p->T : 1) * (size_t)(2 * S + S * S));
   if (!wm || !scratch) { free(wm); free(scratch); return OR_ENOMEM; }
-  newton_ctx c = {p, H, wm, scratch};
+  newton_ctx c = {p, H, wm, scratch, 0};
   int k_done = 0, conv = 0, status = OR_OK;
   for (int k = 0; k < max_iters; ++k) {
+    c.picard = k < picard_iters;
     for (int i = 0; i < nthreads; ++i) wm[i] = 0.0;
     rc = run_channels(p->B * p->D, nthreads, newton_channels, &c);
     if (rc) { status = rc; break; }
@@ -580,13 +645,14 @@ static void vjp_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
   int S = state_size(p->cell), G = gate_count(p->cell);
   int64_t T = p->T, N = p->B * p->T * p->D;
   double* lam = c->scratch + (size_t)worker * (size_t)T * (size_t)S;
-  double u[4], w[4], bias[4], prev[2], sn[2], J[4], dfdu[8], wcoef[4];
+  double u[OR_GMAX], w[OR_GMAX], bias[OR_GMAX], prev[OR_SMAX], sn[OR_SMAX], J[OR_SMAX * OR_SMAX];
+  double dfdu[OR_SMAX * OR_GMAX], wcoef[OR_GMAX];
   for (int64_t ch = ch0; ch < ch1; ++ch) {
     int64_t b = ch / p->D, d = ch % p->D;
     gather_params(p, d, w, bias);
     /* adjoint recurrence, backwards in time */
     for (int64_t t = T - 1; t >= 0; --t) {
-      double acc[2] = {0.0, 0.0};
+      double acc[OR_SMAX] = {0.0, 0.0, 0.0, 0.0};
       acc[S - 1] = (double)c->g[elem_index(p, b, t, d)]; /* e_h g_t */
       if (t + 1 < T && !starts_at(p, t + 1)) {   /* nothing flows back across a sequence start */
         for (int k = 0; k < S; ++k) prev[k] = c->s[traj_index(p, k, b, t, d)];
@@ -664,4 +730,4 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
 }
 
 /* ABI version of this file's entry points, so the wrapper can check it */
-int or_abi_version(void) { return 5; }
+int or_abi_version(void) { return 6; }
