@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PARARNN_ABI_VERSION 3
+#define PARARNN_ABI_VERSION 4
 /* upper bound of Newton iterations per call (report.residual holds one more) */
 #define PARARNN_MAX_ITERS 64
 
@@ -64,8 +64,18 @@ typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
  *              c = tanh(U_c + a_c (r h) + b_c),  h' = (1 - z) h + z c
  *  DIAG_LSTM G=4 (i, f, o, g), S=2 with state (c, h), diagonal recurrent weights acting on h:
  *              i, f, o = sig(U + w h + b),  g = tanh(U_g + w_g h + b_g),
- *              c' = f c + i g,  h' = o tanh(c')                                            */
-typedef enum { PARARNN_CELL_LINEAR = 0, PARARNN_CELL_DIAG_GRU = 1, PARARNN_CELL_DIAG_LSTM = 2 } pararnn_cell;
+ *              c' = f c + i g,  h' = o tanh(c')
+ *  DIAG_SLSTM G=4 (z, i, f, o), S=4 with state (c, n, m, h): the sLSTM that the pararnn-torch
+ *             README names (ParaSLSTM, mix="diag"; "API overview", "Method") in its published
+ *             form, exponential input gate, sigmoid forget gate and log-domain stabiliser m,
+ *             diagonal recurrent weights acting on h:
+ *              u_g = U_g + w_g h + b_g,  z = tanh(u_z),  o = sig(u_o),  lf = log sig(u_f),
+ *              m' = max(lf + m, u_i),  i' = exp(u_i - m'),  f' = exp(lf + m - m'),
+ *              c' = f' c + i' z,  n' = f' n + i',  h' = o c' / n'
+ *             (at a tie of the max the forget branch is taken).  Its Newton iteration wants a few
+ *             Picard sweeps first (opts.picard_iters); it has no measured budget (max_iters > 0). */
+typedef enum { PARARNN_CELL_LINEAR = 0, PARARNN_CELL_DIAG_GRU = 1, PARARNN_CELL_DIAG_LSTM = 2,
+               PARARNN_CELL_DIAG_SLSTM = 3 } pararnn_cell;
 
 typedef struct {
   int32_t cell;          /* pararnn_cell */
@@ -104,6 +114,10 @@ typedef struct {
                               equal s_out (resume from a previous solve's output).                  */
   int32_t final_residual;  /* nonzero: one extra pass computes max|r| of the returned trajectory   */
   int32_t init_mode;       /* pararnn_init_mode; ignored when init_guess is non-NULL                 */
+  int32_t picard_iters;    /* the first min(picard_iters, K) of the K updates are Picard sweeps
+                              H^{k+1}_t = f(H^k_{t-1}, x_t) (the scan element's A set to 0) instead
+                              of Newton updates (pararnn-torch README, "API overview": Picard
+                              iterations warm the first guess); 0..PARARNN_MAX_ITERS             */
 } pararnn_newton_opts;
 
 typedef struct {          /* (host) */

@@ -19,11 +19,11 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
-CELLS = {"linear": 0, "gru": 1, "lstm": 2}
-GATES = {0: 2, 1: 3, 2: 4}
-STATE = {0: 1, 1: 1, 2: 2}
+CELLS = {"linear": 0, "gru": 1, "lstm": 2, "slstm": 3}
+GATES = {0: 2, 1: 3, 2: 4, 3: 4}
+STATE = {0: 1, 1: 1, 2: 2, 3: 4}
 MAX_ITERS = 64
-ABI_VERSION = 3
+ABI_VERSION = 4
 INIT_ZERO, INIT_WARM = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
           -5: "Newton diverged"}
@@ -52,7 +52,7 @@ class _Problem(ctypes.Structure):
 
 class _Opts(ctypes.Structure):
     _fields_ = [("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("init_guess", ctypes.c_void_p),
-                ("final_residual", ctypes.c_int32), ("init_mode", ctypes.c_int32)]
+                ("final_residual", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("picard_iters", ctypes.c_int32)]
 
 
 class _Report(ctypes.Structure):
@@ -207,7 +207,8 @@ def newton_budget(cell, T, warm_start=False, max_iters=None) -> int:
 
 
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
-                 final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None):
+                 final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None,
+                 picard_iters=0):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
@@ -217,6 +218,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     warm_start: without init_guess, start from H^0_t = f(0, x_t) instead of zeros.
     cu_seqlens: int32 [n_seqs + 1] offsets of sequences packed along T (every batch row); each sequence
     after the first starts from the zero state.
+    picard_iters: the first picard_iters of the iterations are Picard sweeps H_t = f(H_{t-1}, x_t).
     on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
     launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
     entry points prepare / iterate / report, which launch exactly the same kernels.
@@ -233,7 +235,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
         raise ValueError("init_guess must be [S, B, T, D]")
     opts = _Opts(int(max_iters or 0), float(tol), init_guess.data_ptr() if init_guess is not None else None,
-                 1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO)
+                 1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO, int(picard_iters))
     nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
     ws = _workspace(nbytes, dev, "newton")
     rep = _Report() if report else None

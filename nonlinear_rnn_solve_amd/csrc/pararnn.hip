@@ -45,7 +45,7 @@
 namespace pr {
 
 constexpr int WAVE = 64;
-enum { CELL_LINEAR = 0, CELL_GRU = 1, CELL_LSTM = 2 };
+enum { CELL_LINEAR = 0, CELL_GRU = 1, CELL_LSTM = 2, CELL_SLSTM = 3 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
 // ------------------------------------------------------------------------------------------------
@@ -53,6 +53,7 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // v_rcp_f32 is 1/x, each about 1 ulp); sigmoid and tanh from their definitions.
 // ------------------------------------------------------------------------------------------------
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 DEV float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 DEV float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 DEV float sigmoid(float x) { return hw_rcp(1.0f + hw_exp2(-kLog2e * x)); }
@@ -659,6 +660,7 @@ template <int CELL> struct CellInfo;
 template <> struct CellInfo<CELL_LINEAR> { static constexpr int S = 1, G = 2; };
 template <> struct CellInfo<CELL_GRU> { static constexpr int S = 1, G = 3; };
 template <> struct CellInfo<CELL_LSTM> { static constexpr int S = 2, G = 4; };
+template <> struct CellInfo<CELL_SLSTM> { static constexpr int S = 4, G = 4; };
 
 // Per-lane channel parameters for V channels: the recurrent weights w and biases b, and the same
 // two scaled by the exponent factor of their gate (-log2(e) for a sigmoid gate, 2 log2(e) for a tanh
@@ -670,6 +672,7 @@ struct Params {
 template <int CELL> DEV float gate_scale(int g);
 template <> DEV float gate_scale<CELL_GRU>(int g) { return g == 2 ? 2.0f * kLog2e : -kLog2e; }     // z, r, c
 template <> DEV float gate_scale<CELL_LSTM>(int g) { return g == 3 ? 2.0f * kLog2e : -kLog2e; }    // i, f, o, g
+template <> DEV float gate_scale<CELL_SLSTM>(int) { return 1.0f; }   // used unscaled (log domain)
 template <> DEV float gate_scale<CELL_LINEAR>(int) { return 0.0f; }
 
 template <int CELL, int G, int V>
@@ -742,6 +745,75 @@ DEV LstmPart lstm_eval(const Params<G, V>& pm, int v, float ui, float uf, float 
   p.J01 = dc_dh;
   p.J10 = p.kh * fg;
   p.J11 = fmaf(p.dh_o, pm.w[2][v], p.kh * dc_dh);
+  return p;
+}
+
+// sLSTM, diagonal recurrence, state (c, n, m, h), gates z, i, f, o (the published sLSTM with
+// exponential input gate, sigmoid forget gate and log-domain stabiliser m):
+//   u_g = U_g + w_g h + b_g, z = tanh(u_z), o = sig(u_o), lf = log sig(u_f),
+//   m' = max(lf + m, u_i), i' = exp(u_i - m'), f' = exp(lf + m - m'),
+//   c' = f' c + i' z, n' = f' n + i', h' = o c' / n'.
+// At a tie of the max the forget branch is taken (its derivative is the branch's).
+// J is row-major over (c, n, m, h); d[i][g] = d s'_i / d u_g (gate order z, i, f, o).
+struct SlstmPart {
+  float s2[4];
+  float J[16];
+  float d[16];
+};
+template <int G, int V>
+DEV SlstmPart slstm_eval(const Params<G, V>& pm, int v, float Uz, float Ui, float Uf, float Uo, float c, float n,
+                         float m, float h) {
+  SlstmPart p;
+  const float uz = fmaf(pm.w[0][v], h, Uz + pm.bias[0][v]);
+  const float ui = fmaf(pm.w[1][v], h, Ui + pm.bias[1][v]);
+  const float uf = fmaf(pm.w[2][v], h, Uf + pm.bias[2][v]);
+  const float uo = fmaf(pm.w[3][v], h, Uo + pm.bias[3][v]);
+  const float z = tanh_x(2.0f * kLog2e * uz);
+  const float o = sig_x(-kLog2e * uo);
+  // log sig(u_f) = min(u_f, 0) - log(1 + e^{-|u_f|}); d/du_f = sig(-u_f)
+  const float e = hw_exp2(-kLog2e * fabsf(uf));
+  const float lf = fminf(uf, 0.0f) - kLn2 * __builtin_amdgcn_logf(1.0f + e);
+  const float dlf = uf >= 0.0f ? e * hw_rcp(1.0f + e) : hw_rcp(1.0f + e);
+  const float lfm = lf + m;
+  const bool fb = lfm >= ui;
+  const float m2 = fb ? lfm : ui;
+  const float ip = hw_exp2(kLog2e * (ui - m2)), fp = hw_exp2(kLog2e * (lfm - m2));
+  const float c2 = fmaf(fp, c, ip * z), n2 = fmaf(fp, n, ip);
+  const float rn = hw_rcp(n2);
+  const float hn = c2 * rn;                 // c' / n'
+  p.s2[0] = c2; p.s2[1] = n2; p.s2[2] = m2; p.s2[3] = o * hn;
+  // i', f', m' as functions of (u_i, u_f, m) on the active branch
+  const float dm_ui = fb ? 0.0f : 1.0f, dm_uf = fb ? dlf : 0.0f, dm_m = fb ? 1.0f : 0.0f;
+  const float dip_ui = ip * (1.0f - dm_ui), dip_uf = -ip * dm_uf, dip_m = -ip * dm_m;
+  const float dfp_ui = -fp * dm_ui, dfp_uf = fp * (dlf - dm_uf), dfp_m = fp * (1.0f - dm_m);
+  const float dc[4] = {ip * fmaf(-z, z, 1.0f), fmaf(c, dfp_ui, z * dip_ui), fmaf(c, dfp_uf, z * dip_uf), 0.0f};
+  const float dn[4] = {0.0f, fmaf(n, dfp_ui, dip_ui), fmaf(n, dfp_uf, dip_uf), 0.0f};
+  const float dm[4] = {0.0f, dm_ui, dm_uf, 0.0f};
+  const float orn = o * rn;
+  float dh[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) dh[g] = orn * fmaf(-hn, dn[g], dc[g]);   // o (dc n' - c' dn) / n'^2
+  dh[3] += hn * fmaf(-o, o, o);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    p.d[0 * 4 + g] = dc[g]; p.d[1 * 4 + g] = dn[g]; p.d[2 * 4 + g] = dm[g]; p.d[3 * 4 + g] = dh[g];
+  }
+  const float dc_m = fmaf(c, dfp_m, z * dip_m), dn_m = fmaf(n, dfp_m, dip_m);
+  float sc = 0.0f, sn = 0.0f, sm = 0.0f, sh = 0.0f;   // h enters every gate through w_g h
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    sc = fmaf(dc[g], pm.w[g][v], sc);
+    sn = fmaf(dn[g], pm.w[g][v], sn);
+    sm = fmaf(dm[g], pm.w[g][v], sm);
+    sh = fmaf(dh[g], pm.w[g][v], sh);
+  }
+  p.J[0] = fp;   p.J[1] = 0.0f; p.J[2] = dc_m;  p.J[3] = sc;
+  p.J[4] = 0.0f; p.J[5] = fp;   p.J[6] = dn_m;  p.J[7] = sn;
+  p.J[8] = 0.0f; p.J[9] = 0.0f; p.J[10] = dm_m; p.J[11] = sm;
+  p.J[12] = orn * fp;                       // d h' / d c
+  p.J[13] = -orn * hn * fp;                 // d h' / d n
+  p.J[14] = orn * fmaf(-hn, dn_m, dc_m);    // d h' / d m
+  p.J[15] = sh;
   return p;
 }
 
@@ -879,6 +951,7 @@ struct NewtonOp {
     const float* h_in;        // H^k [S][B][T][D], or NULL for H^k = 0 (or the warm start)
     float* h_out;             // H^{k+1}; may equal h_in
     int32_t warm;             // h_in == NULL: H^0_t = f(0, x_t) computed here instead of 0
+    int32_t picard;           // this launch is a Picard sweep: H^{k+1}_t = f(H^k_{t-1}, x_t) (A = 0)
     uint32_t* res_slot;       // max |r| of this iteration (float bits, atomicMax)
     const uint32_t* res_hist; // max |r| of earlier iterations
     int32_t k;
@@ -900,7 +973,8 @@ struct NewtonOp {
     load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
   }
   static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
-    return tl.nvalid == L ? produce_t<false>(a, tl, ln) : produce_t<true>(a, tl, ln);
+    if (a.picard) return tl.nvalid == L ? produce_t<false, true>(a, tl, ln) : produce_t<true, true>(a, tl, ln);
+    return tl.nvalid == L ? produce_t<false, false>(a, tl, ln) : produce_t<true, false>(a, tl, ln);
   }
   // f(0, u) for channel slot v (pararnn-torch README, "Method": the GRU / LSTM warm start)
   static DEV void warm_state(const Params<G, V>& pm, int v, const float (&u)[G][V], float (&o)[S]) {
@@ -908,13 +982,17 @@ struct NewtonOp {
       o[0] = u[1][v];
     } else if constexpr (CELL == CELL_GRU) {
       o[0] = gru_eval(pm, v, u[0][v], u[1][v], u[2][v], 0.0f).f;
-    } else {
+    } else if constexpr (CELL == CELL_LSTM) {
       const LstmPart q = lstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], 0.0f, 0.0f);
       o[0] = q.c2;
       o[1] = q.h2;
+    } else {
+      const SlstmPart q = slstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], 0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int k = 0; k < S; ++k) o[k] = q.s2[k];
     }
   }
-  template <bool MASKED>
+  template <bool MASKED, bool PIC>
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
     const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
     const Common& c = a.c;
@@ -1046,31 +1124,52 @@ struct NewtonOp {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         Aff<S> e;
+        // a Picard sweep keeps f and drops the Jacobian: the element is (0, f)
         if constexpr (CELL == CELL_LINEAR) {
           const float hp = rs ? 0.0f : h[0][i][v];
           const float f = fmaf(u[0][i][v], hp, u[1][i][v]);
           if (ok) rm.add(h[0][i + 1][v] - f);
-          e.A[0] = rs ? 0.0f : u[0][i][v];
-          e.b[0] = u[1][i][v];
+          e.A[0] = (rs || PIC) ? 0.0f : u[0][i][v];
+          e.b[0] = PIC ? f : u[1][i][v];
         } else if constexpr (CELL == CELL_GRU) {
           const float hp = rs ? 0.0f : h[0][i][v];
           const GruOut q = gru_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], hp);
           if (ok) rm.add(h[0][i + 1][v] - q.f);
-          e.A[0] = rs ? 0.0f : q.J;
-          e.b[0] = fmaf(-q.J, hp, q.f);
-        } else {
+          e.A[0] = (rs || PIC) ? 0.0f : q.J;
+          e.b[0] = PIC ? q.f : fmaf(-q.J, hp, q.f);
+        } else if constexpr (CELL == CELL_LSTM) {
           const float cp = rs ? 0.0f : h[0][i][v], hp = rs ? 0.0f : h[1][i][v];
           const LstmPart q = lstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], cp, hp);
           if (ok) {
             rm.add(h[0][i + 1][v] - q.c2);
             rm.add(h[1][i + 1][v] - q.h2);
           }
-          e.A[0] = rs ? 0.0f : q.J00;
-          e.A[1] = rs ? 0.0f : q.J01;
-          e.A[2] = rs ? 0.0f : q.J10;
-          e.A[3] = rs ? 0.0f : q.J11;
-          e.b[0] = q.c2 - fmaf(q.J00, cp, q.J01 * hp);
-          e.b[1] = q.h2 - fmaf(q.J10, cp, q.J11 * hp);
+          e.A[0] = (rs || PIC) ? 0.0f : q.J00;
+          e.A[1] = (rs || PIC) ? 0.0f : q.J01;
+          e.A[2] = (rs || PIC) ? 0.0f : q.J10;
+          e.A[3] = (rs || PIC) ? 0.0f : q.J11;
+          e.b[0] = PIC ? q.c2 : q.c2 - fmaf(q.J00, cp, q.J01 * hp);
+          e.b[1] = PIC ? q.h2 : q.h2 - fmaf(q.J10, cp, q.J11 * hp);
+        } else {
+          float sp[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sp[k] = rs ? 0.0f : h[k][i][v];
+          const SlstmPart q = slstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], sp[0], sp[1],
+                                         sp[2], sp[3]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (ok) rm.add(h[k][i + 1][v] - q.s2[k]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) e.A[k] = (rs || PIC) ? 0.0f : q.J[k];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float acc = q.s2[r];
+            if (!PIC) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) acc = fmaf(-q.J[r * 4 + k], sp[k], acc);
+            }
+            e.b[r] = acc;
+          }
         }
         if (MASKED) {
           const Aff<S> one = aff_id<S>();
@@ -1115,6 +1214,7 @@ template <int CELL> struct VjpStash;
 template <> struct VjpStash<CELL_LINEAR> { float hp; };
 template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
 template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
+template <> struct VjpStash<CELL_SLSTM> { float d[16]; float hp; };
 
 template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct VjpOp {
@@ -1227,12 +1327,21 @@ struct VjpOp {
           st.pc = q.pc;
           st.hp = sp[0][e][v];
           st.r = q.r;
-        } else {
+        } else if constexpr (CELL == CELL_LSTM) {
           const LstmPart q = lstm_eval(pm, v, u[0][e][v], u[1][e][v], u[2][e][v], u[3][e][v], sp[0][e][v],
                                        sp[1][e][v]);
           J[0] = q.J00; J[1] = q.J01; J[2] = q.J10; J[3] = q.J11;
           st.dci = q.dc_i; st.dcf = q.dc_f; st.dcg = q.dc_g; st.dho = q.dh_o; st.kh = q.kh;
           st.hp = sp[1][e][v];
+        } else {
+          const SlstmPart q = slstm_eval(pm, v, u[0][e][v], u[1][e][v], u[2][e][v], u[3][e][v], sp[0][e][v],
+                                         sp[1][e][v], sp[2][e][v], sp[3][e][v]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            J[k] = q.J[k];
+            st.d[k] = q.d[k];
+          }
+          st.hp = sp[3][e][v];
         }
         if (e < L) {
           const bool okl = !MASKED || e < tl.nvalid;
@@ -1295,7 +1404,7 @@ struct VjpOp {
             par[v][2] = fmaf(du[2][v], st.r * st.hp, par[v][2]);
 #pragma unroll
             for (int g = 0; g < 3; ++g) par[v][3 + g] += du[g][v];
-          } else {
+          } else if constexpr (CELL == CELL_LSTM) {
             const float lc = x[v][0], lh = x[v][1];
             const float m = fmaf(st.kh, lh, lc);   // lambda_c + kh lambda_h
             du[0][v] = m * st.dci;
@@ -1306,6 +1415,17 @@ struct VjpOp {
             for (int g = 0; g < 4; ++g) {
               par[v][g] = fmaf(du[g][v], st.hp, par[v][g]);
               par[v][4 + g] += du[g][v];
+            }
+          } else {
+            // dU_g = sum_i lambda_i d s'_i / d u_g; every gate's w multiplies h_{t-1}
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float acc = 0.0f;
+#pragma unroll
+              for (int i2 = 0; i2 < 4; ++i2) acc = fmaf(x[v][i2], st.d[i2 * 4 + g], acc);
+              du[g][v] = acc;
+              par[v][g] = fmaf(acc, st.hp, par[v][g]);
+              par[v][4 + g] += acc;
             }
           }
           if (t == 0 && a.d_s0) {
@@ -1450,10 +1570,15 @@ __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1
         } else if constexpr (CELL == CELL_GRU) {
           const GruOut q = gru_eval(pm, v, u[0][v], u[1][v], u[2][v], prev[0][v]);
           m = nanmax(m, fabsf(cur[0][v] - q.f));
-        } else {
+        } else if constexpr (CELL == CELL_LSTM) {
           const LstmPart q = lstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], prev[0][v], prev[1][v]);
           m = nanmax(m, fabsf(cur[0][v] - q.c2));
           m = nanmax(m, fabsf(cur[1][v] - q.h2));
+        } else {
+          const SlstmPart q = slstm_eval(pm, v, u[0][v], u[1][v], u[2][v], u[3][v], prev[0][v], prev[1][v],
+                                         prev[2][v], prev[3][v]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m = nanmax(m, fabsf(cur[k][v] - q.s2[k]));
         }
       }
     }
@@ -1480,8 +1605,8 @@ uint32_t next_tag() {
   return t;
 }
 
-int state_size(int cell) { return cell == CELL_LSTM ? 2 : 1; }
-int gate_count(int cell) { return cell == CELL_LSTM ? 4 : (cell == CELL_GRU ? 3 : 2); }
+int state_size(int cell) { return cell == CELL_SLSTM ? 4 : (cell == CELL_LSTM ? 2 : 1); }
+int gate_count(int cell) { return (cell == CELL_LSTM || cell == CELL_SLSTM) ? 4 : (cell == CELL_GRU ? 3 : 2); }
 
 // workspace: [header 4 KiB: tickets, residual slots][packed-sequence mask][look-back words]
 // [VJP partials]; the mask is (T >> 5) + 2 words (read two at a time by seg_bits)
@@ -1533,6 +1658,12 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t 
 #ifndef PR_VJP_GRU_CFG
 #define PR_VJP_GRU_CFG 1, 8, 16, 4, 1
 #endif
+#ifndef PR_SLSTM_CFG
+#define PR_SLSTM_CFG 1, 2, 4, 2, 4
+#endif
+#ifndef PR_VJP_SLSTM_CFG
+#define PR_VJP_SLSTM_CFG 1, 2, 4, 2, 4
+#endif
 #ifndef PR_VJP_LSTM_CFG
 #define PR_VJP_LSTM_CFG 1, 4, 16, 4, 1
 #endif
@@ -1540,10 +1671,12 @@ template <int V_, int L_, int NW_, int MINW_, int TS_>
 struct TileCfg { static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_; };
 template <int CELL> struct NewtonCfg : TileCfg<PR_GRU_CFG> {};
 template <> struct NewtonCfg<CELL_LSTM> : TileCfg<PR_LSTM_CFG> {};
+template <> struct NewtonCfg<CELL_SLSTM> : TileCfg<PR_SLSTM_CFG> {};
 template <int S> struct ScanCfg : TileCfg<PR_SCAN1_CFG> {};
 template <> struct ScanCfg<2> : TileCfg<PR_SCAN2_CFG> {};
 template <int CELL> struct VjpCfg : TileCfg<PR_VJP_GRU_CFG> {};
 template <> struct VjpCfg<CELL_LSTM> : TileCfg<PR_VJP_LSTM_CFG> {};
+template <> struct VjpCfg<CELL_SLSTM> : TileCfg<PR_VJP_SLSTM_CFG> {};
 
 Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int ticket_slot) {
   Common c;
@@ -1600,7 +1733,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 pararnn_status check_problem(const pararnn_problem* pb) {
   if (!pb) return PARARNN_ERR_INVALID_ARG;
-  if (pb->cell < 0 || pb->cell > 2) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cell < CELL_LINEAR || pb->cell > CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;
   if (pb->pre_dtype != PARARNN_F32 && pb->pre_dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
   if (pb->B < 0 || pb->T < 0 || pb->D < 0) return PARARNN_ERR_INVALID_ARG;
   if (pb->B > (int64_t(1) << 40) || pb->D > (int64_t(1) << 40)) return PARARNN_ERR_INVALID_ARG;
@@ -1650,6 +1783,7 @@ struct NewtonKernel {
     a.h_in = (k == 0) ? op->init_guess : s_out;
     a.h_out = s_out;
     a.warm = op->init_mode == PARARNN_INIT_WARM;
+    a.picard = k < op->picard_iters ? 1 : 0;
     a.res_slot = res + k;
     a.res_hist = res;
     a.k = k;
@@ -1695,6 +1829,7 @@ NewtonEntry pick_newton(const pararnn_problem* pb) {
   const bool seg = pb->cu_seqlens != nullptr;
   if (pb->cell == CELL_GRU) return newton_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
   if (pb->cell == CELL_LSTM) return newton_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
+  if (pb->cell == CELL_SLSTM) return newton_entry_dt<CELL_SLSTM>(pb->pre_dtype, seg);
   return newton_entry_dt<CELL_LINEAR>(pb->pre_dtype, seg);
 }
 
@@ -1819,6 +1954,7 @@ VjpEntry pick_vjp(const pararnn_problem* pb) {
   const bool seg = pb->cu_seqlens != nullptr;
   if (pb->cell == CELL_GRU) return vjp_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
   if (pb->cell == CELL_LSTM) return vjp_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
+  if (pb->cell == CELL_SLSTM) return vjp_entry_dt<CELL_SLSTM>(pb->pre_dtype, seg);
   return vjp_entry_dt<CELL_LINEAR>(pb->pre_dtype, seg);
 }
 
@@ -1895,6 +2031,8 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   if (rc) return rc;
   if (!op || op->max_iters < 0 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
   if (op->init_mode != PARARNN_INIT_ZERO && op->init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
+  if (op->picard_iters < 0 || op->picard_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (op->max_iters == 0 && pb->cell == CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;   // no measured budget
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
@@ -1978,8 +2116,9 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
 }
 
 int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {
-  if (cell < CELL_LINEAR || cell > CELL_LSTM || T < 0 || max_iters < 0 || max_iters > PARARNN_MAX_ITERS)
+  if (cell < CELL_LINEAR || cell > CELL_SLSTM || T < 0 || max_iters < 0 || max_iters > PARARNN_MAX_ITERS)
     return PARARNN_ERR_INVALID_ARG;
+  if (max_iters == 0 && cell == CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;   // no measured budget
   if (init_mode != PARARNN_INIT_ZERO && init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   return max_iters > 0 ? max_iters : auto_iters(cell, init_mode, T);
 }

@@ -40,11 +40,12 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
                    ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0),'
                    ' offsetof(pararnn_problem, cu_seqlens), offsetof(pararnn_problem, n_seqs),'
                    ' sizeof(pararnn_newton_opts),'
                    ' offsetof(pararnn_newton_opts, final_residual), offsetof(pararnn_newton_opts, init_mode),'
+                   ' offsetof(pararnn_newton_opts, picard_iters),'
                    ' sizeof(pararnn_report),'
                    ' offsetof(pararnn_report, residual)); return 0;}\n')
     exe = tmp_path / "layout"
@@ -53,6 +54,7 @@ def test_struct_layouts_match_header(tmp_path):
     want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
             api._Problem.cu_seqlens.offset, api._Problem.n_seqs.offset,
             ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, api._Opts.init_mode.offset,
+            api._Opts.picard_iters.offset,
             ctypes.sizeof(api._Report),
             api._Report.residual.offset]
     assert got == want
@@ -101,6 +103,8 @@ def test_validation_codes_without_launching(lib):
     assert solve(_problem(), o=api._Opts(-1, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
+    assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 0, -1)) == -1   # negative Picard count
+    assert solve(_problem(cell=3), o=api._Opts(0, 0.0, None, 0)) == -1   # sLSTM has no measured budget
     p = _problem()
     p.cu_seqlens, p.n_seqs = 4098, 3                          # offsets not 4-byte aligned
     assert solve(p) == -1
@@ -130,7 +134,7 @@ def test_validation_codes_without_launching(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.pararnn_status_string(s).decode() != "unknown status"
-    assert lib.pararnn_abi_version() == api.ABI_VERSION == 3
+    assert lib.pararnn_abi_version() == api.ABI_VERSION == 4
 
 
 def test_binding_refuses_cpu_tensors():
@@ -158,7 +162,9 @@ def test_automatic_budget_is_the_measured_kstar(lib):
     assert lib.pararnn_newton_budget(0, 0, 10 ** 9, 0) == 1          # LINEAR: one exact scan
     assert lib.pararnn_newton_budget(1, 0, 100, 5) == 5              # an explicit budget wins
     assert lib.pararnn_newton_budget(1, 2, 100, 0) == -1
-    assert lib.pararnn_newton_budget(3, 0, 100, 0) == -1
+    assert lib.pararnn_newton_budget(3, 0, 100, 0) == -1          # sLSTM: no measured budget
+    assert lib.pararnn_newton_budget(3, 0, 100, 7) == 7
+    assert lib.pararnn_newton_budget(4, 0, 100, 0) == -1
     assert lib.pararnn_newton_budget(1, 0, -1, 0) == -1
     assert lib.pararnn_newton_budget(1, 0, 100, 65) == -1
     assert api.newton_budget("gru", 4096) == lib.pararnn_newton_budget(1, 0, 4096, 0)
