@@ -95,6 +95,7 @@ def main():
     ap.add_argument("--cpu-channels", type=int, default=0, help="channels in the CPU-baseline sample (0: auto)")
     ap.add_argument("--variants", action="store_true", help="time warm start / K* budget / packed variants")
     ap.add_argument("--kstar", action="store_true", help="time the automatic budget over a grid of lengths")
+    ap.add_argument("--slstm", action="store_true", help="time the diagonal sLSTM solve and VJP over a grid of lengths")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many MiB "
                          "(same-box bandwidth context, and the known-size kernel that calibrates HBM counters)")
@@ -117,6 +118,9 @@ def main():
         return
     if args.kstar:
         kstar_bench(torch, dev, args)
+        return
+    if args.slstm:
+        slstm_bench(torch, dev, args)
         return
     wl = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(wl)
@@ -308,6 +312,37 @@ def kstar_bench(torch, dev, args):
                                   "channel_tokens_per_s": T * 1024 * iters / (ms * 1e-3)}), flush=True)
             del pre, out
             torch.cuda.empty_cache()
+
+
+def slstm_bench(torch, dev, args):
+    """The diagonal sLSTM (fp32, B=8, D=256, as in the pararnn-torch README's sLSTM benchmark) over a
+    grid of lengths: 8 Picard sweeps, then Newton until the max residual is below 1e-5 (at most 40
+    iterations in all), then the VJP.  One JSON line per length."""
+    from nonlinear_rnn_solve_amd import api, synth
+    B, D = 8, 256
+    per_elem = 4 * 4 + 4 * 4 + 4 * 4          # U (4 planes) + (c, n, m, h)^k + (c, n, m, h)^{k+1}
+    for T in (1024, 4096, 16384, 65536):
+        inp = synth.make_inputs("slstm", B, T, D, seed=4000 + T // 1024, with_grad=True)
+        pre, w, b, g = device_inputs(torch, dev, inp)
+        out = torch.empty((4, B, T, D), dtype=torch.float32, device=dev)
+        ms, iters, kern = time_solve(torch, api, "slstm", pre, w, b, g, out, args.steps, args.warmup, vjp=True,
+                                     max_iters=40, tol=1e-5, picard_iters=8)
+        _, rep_ = api.newton_solve("slstm", pre, w, b, out=out, max_iters=40, tol=1e-5, picard_iters=8,
+                                   final_residual=True)
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.scan_vjp("slstm", pre, out, g, w, b, want_s0=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        N = B * T * D
+        print(json.dumps({"cell": "slstm", "storage": "f32", "B": B, "T": T, "D": D, "picard": 8, "tol": 1e-5,
+                          "iters": iters, "converged": rep_.converged, "final_residual": rep_.final_residual,
+                          "ms_per_solve_and_vjp": ms, "iteration_kernel_ms": kern,
+                          "iteration_gbs": per_elem * N / (kern * 1e-3) / 1e9, "vjp_ms": e0.elapsed_time(e1),
+                          "channel_tokens_per_s": N * iters / (ms * 1e-3)}), flush=True)
+        del pre, out, g
+        torch.cuda.empty_cache()
 
 
 def copy_bench(torch, dev, args):
