@@ -852,7 +852,7 @@ struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = REV, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   struct Args {
     Common c;
     const void* a;
@@ -941,7 +941,7 @@ struct NewtonOp {
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   struct Args {
     Common c;
     const void* pre[4];
@@ -1222,7 +1222,7 @@ struct VjpOp {
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = true, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : 2;
+  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
   struct Args {
     Common c;
@@ -1659,10 +1659,10 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t 
 #define PR_VJP_GRU_CFG 1, 8, 16, 4, 1
 #endif
 #ifndef PR_SLSTM_CFG
-#define PR_SLSTM_CFG 1, 2, 4, 2, 4
+#define PR_SLSTM_CFG 1, 8, 4, 1, 2
 #endif
 #ifndef PR_VJP_SLSTM_CFG
-#define PR_VJP_SLSTM_CFG 1, 2, 4, 2, 4
+#define PR_VJP_SLSTM_CFG 1, 4, 4, 1, 4
 #endif
 #ifndef PR_VJP_LSTM_CFG
 #define PR_VJP_LSTM_CFG 1, 4, 16, 4, 1
