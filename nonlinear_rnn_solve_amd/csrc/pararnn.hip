@@ -1098,18 +1098,33 @@ struct NewtonOp {
             st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, HALO + k, q0 + v), c.tag, h[k][L][v]);
       }
       if (tl.first_seg && tl.t_lo != 0) {
+        // every halo word of the lane in flight at once (one memory round trip, not one per word);
+        // the predecessor publishes them right after its loads, so a retry is rare
+        uint64_t wv[V][S];
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int k = 0; k < S; ++k) {
-            const uint64_t* wp = word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, HALO + k, q0 + v);
-            uint64_t wv = ld_word(wp);
-            while (!word_ok(wv, c.tag)) {
-              __builtin_amdgcn_s_sleep(1);
-              wv = ld_word(wp);
-            }
-            h[k][0][v] = word_val(wv);
+          for (int k = 0; k < S; ++k) wv[v][k] = ld_word(word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, HALO + k, q0 + v));
+        bool ok = false;
+        while (!ok) {
+          ok = true;
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int k = 0; k < S; ++k) ok = ok && word_ok(wv[v][k], c.tag);
+          if (!ok) {
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+              for (int k = 0; k < S; ++k)
+                if (!word_ok(wv[v][k], c.tag)) wv[v][k] = ld_word(word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, HALO + k, q0 + v));
           }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S; ++k) h[k][0][v] = word_val(wv[v][k]);
       }
     }
     // packed sequences: a step that begins a sequence starts from the zero state, so its previous
