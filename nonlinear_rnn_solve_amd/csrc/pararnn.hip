@@ -1505,35 +1505,51 @@ __global__ void k_segmask(const int32_t* cu, int64_t n, int64_t T, uint32_t* mas
 //   out[j][d] = sum over rows r = (b, chunk) of partial[chunk][j][b*D + d]
 // A workgroup owns 64 consecutive outputs; its 16 row groups each add every 16th row, then the 16
 // partial sums are added in row-group order (bitwise reproducible).
-constexpr int kRedCols = 64, kRedRows = 16;
-__global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce(const float* partial, int64_t n_chunks, int npar,
-                                                                     int64_t B, int64_t D, float* d_w, float* d_bias,
-                                                                     int G) {
+// Parameter gradients from the per-tile partials [n_chunks][npar][B*D] in a fixed order (bitwise
+// reproducible): stage 1 splits the B*n_chunks rows into kRedSlices contiguous slices and sums each
+// slice per output (rows in ascending order within kRedRows interleaved groups, the groups in order);
+// stage 2 sums the slices in order and writes d_w / d_bias.
+constexpr int kRedCols = 64, kRedRows = 4, kRedSlices = 32;
+__global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce1(const float* partial, int64_t n_chunks,
+                                                                      int npar, int64_t B, int64_t D,
+                                                                      float* slices) {
   __shared__ float sh[kRedRows][kRedCols];
   const int col = threadIdx.x % kRedCols, rg = threadIdx.x / kRedCols;
   const int64_t o = static_cast<int64_t>(blockIdx.x) * kRedCols + col;   // output index j*D + d
-  const int64_t C = B * D, R = B * n_chunks;
+  const int64_t C = B * D, R = B * n_chunks, n_out = npar * D;
+  const int64_t per = (R + kRedSlices - 1) / kRedSlices;
+  const int64_t r0 = blockIdx.y * per, r1 = r0 + per < R ? r0 + per : R;
   float sum = 0.0f;
-  if (o < npar * D) {
+  if (o < n_out) {
     const int j = static_cast<int>(o / D);
     const int64_t d = o - j * D;
-    for (int64_t r = rg; r < R; r += kRedRows) {
+    for (int64_t r = r0 + rg; r < r1; r += kRedRows) {
       const int64_t b = r / n_chunks, ch = r - b * n_chunks;
       sum += partial[(ch * npar + j) * C + b * D + d];
     }
   }
   sh[rg][col] = sum;
   __syncthreads();
-  if (rg == 0 && o < npar * D) {
+  if (rg == 0 && o < n_out) {
     float t = 0.0f;
+#pragma unroll
     for (int i = 0; i < kRedRows; ++i) t += sh[i][col];
-    const int j = static_cast<int>(o / D);
-    const int64_t d = o - j * D;
-    if (j < G) {
-      if (d_w) d_w[j * D + d] = t;
-    } else {
-      if (d_bias) d_bias[(j - G) * D + d] = t;
-    }
+    slices[blockIdx.y * n_out + o] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_param_reduce2(const float* slices, int npar, int64_t D, float* d_w,
+                                                      float* d_bias, int G) {
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, n_out = npar * D;
+  if (o >= n_out) return;
+  float t = 0.0f;
+  for (int i = 0; i < kRedSlices; ++i) t += slices[i * n_out + o];
+  const int j = static_cast<int>(o / D);
+  const int64_t d = o - j * D;
+  if (j < G) {
+    if (d_w) d_w[j * D + d] = t;
+  } else {
+    if (d_bias) d_bias[(j - G) * D + d] = t;
   }
 }
 
@@ -1907,9 +1923,12 @@ struct VjpKernel {
   static size_t part_bytes(const Geo& g, const pararnn_problem* pb) {
     return static_cast<size_t>(g.n_chunks) * Op::NPAR * pb->B * pb->D * sizeof(float);
   }
+  static size_t slice_bytes(const pararnn_problem* pb) {
+    return static_cast<size_t>(kRedSlices) * Op::NPAR * pb->D * sizeof(float);
+  }
   static size_t ws(const pararnn_problem* pb) {
     const Geo g = geo(pb);
-    return lb_offset(pb->T) + align256(g.lb_bytes()) + align256(part_bytes(g, pb));
+    return lb_offset(pb->T) + align256(g.lb_bytes()) + align256(part_bytes(g, pb)) + align256(slice_bytes(pb));
   }
   static pararnn_status run(const pararnn_problem* pb, const float* s, const float* gr, float* d_pre, float* d_w,
                             float* d_bias, float* d_s0, float* lam, void* ws, hipStream_t st) {
@@ -1938,9 +1957,12 @@ struct VjpKernel {
     if constexpr (Op::NPAR > 0) {
       if (d_w || d_bias) {
         const int64_t n = Op::NPAR * pb->D;
-        hipLaunchKernelGGL(k_param_reduce, dim3(static_cast<unsigned>((n + kRedCols - 1) / kRedCols)),
-                           dim3(kRedCols * kRedRows), 0, st,
-                           a.partial, g.n_chunks, Op::NPAR, pb->B, pb->D, d_w, d_bias, Op::G);
+        float* slices = reinterpret_cast<float*>(reinterpret_cast<char*>(a.partial) + align256(part_bytes(g, pb)));
+        hipLaunchKernelGGL(k_param_reduce1, dim3(static_cast<unsigned>((n + kRedCols - 1) / kRedCols), kRedSlices),
+                           dim3(kRedCols * kRedRows), 0, st, a.partial, g.n_chunks, Op::NPAR, pb->B, pb->D, slices);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+        hipLaunchKernelGGL(k_param_reduce2, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, slices,
+                           Op::NPAR, pb->D, d_w, d_bias, Op::G);
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
       }
     }
