@@ -152,7 +152,11 @@ def main():
 
     vjp_events = []
 
-    def step(record):
+    # Timed steps are enqueued back to back with no host synchronisation (as a training loop would run
+    # them): the iteration count is taken from a reported solve before and after the timed region (the
+    # solve is deterministic, so every step runs the same launches), and the per-launch HIP events
+    # recorded in the timed region give the kernel durations.
+    def step(record, report=False):
         rec = []
         if wl.cell == "linear":
             e0 = torch.cuda.Event(enable_timing=True)
@@ -164,8 +168,8 @@ def main():
             iters = 1
         else:
             _, rep = api.newton_solve(wl.cell, pre, w, b, max_iters=wl.max_iters, tol=wl.tol, out=out,
-                                      on_iteration=lambda k, ph: hook(k, ph, rec))
-            iters = rep.iters
+                                      on_iteration=lambda k, ph: hook(k, ph, rec), report=report)
+            iters = rep.iters if rep is not None else None
             if wl.vjp:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -179,14 +183,17 @@ def main():
         return iters
 
     for _ in range(args.warmup):
-        iters = step(False)
+        step(False)
+    iters = step(False, report=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        iters = step(True)
+        step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    if step(False, report=True) != iters:
+        raise RuntimeError("the iteration count changed between steps")
 
     # dominant kernel: the steady-state fused Newton iteration (k >= 1 and doing work), or the scan
     durs = []
@@ -238,7 +245,7 @@ def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **
     stream = torch.cuda.current_stream(out.device)
     recs = []
 
-    def one(record):
+    def one(record, report=False):
         rec = []
 
         def hook(k, phase):
@@ -248,20 +255,23 @@ def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **
                 rec.append([k, ev, None])
             else:
                 rec[-1][2] = ev
-        _, rep_ = api.newton_solve(cell, pre, w, b, out=out, on_iteration=hook, **opts)
+        _, rep_ = api.newton_solve(cell, pre, w, b, out=out, on_iteration=hook, report=report, **opts)
         if vjp:
             api.scan_vjp(cell, pre, out, g, w, b, want_s0=False, cu_seqlens=opts.get("cu_seqlens"))
         if record:
             recs.append(rec)
-        return rep_.iters
+        return rep_.iters if rep_ is not None else None
     for _ in range(warmup):
         one(False)
+    iters = one(False, report=True)       # the solve is deterministic: every timed step runs these launches
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        iters = one(True)
+        one(True)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    if one(False, report=True) != iters:
+        raise RuntimeError("the iteration count changed between solves")
     # steady-state iterations (k >= 1) when there are any: iteration 0 of a zero start reads no iterate
     durs = [e0.elapsed_time(e1) for rec in recs for k, e0, e1 in rec if (1 if iters > 1 else 0) <= k < iters]
     return ms, iters, float(np.mean(durs))
