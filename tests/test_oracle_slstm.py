@@ -207,3 +207,22 @@ def test_vjp_matches_autograd():
     np.testing.assert_allclose(got["d_bias"], b.grad.numpy(), rtol=1e-9, atol=1e-11)
     np.testing.assert_allclose(got["d_s0"], s0t.grad.numpy(), rtol=1e-9, atol=1e-11)
     np.testing.assert_allclose(got["lam"][3], np.stack([x.grad.numpy() for x in hs], 1), rtol=1e-9, atol=1e-11)
+
+
+def test_stabiliser_is_the_running_maximum_also_near_ties():
+    # m' = max(log sig(u_f) + m, u_i) exactly, including within a hair of the tie (where only the
+    # representation (c, n, m), not h, would notice a wrong branch)
+    rng = np.random.default_rng(1035)
+    w = np.zeros(4)
+    bias = np.zeros(4)
+    for trial in range(200):
+        u = rng.normal(0, 1, 4)
+        s = np.array([rng.normal(), abs(rng.normal()) + 0.3, rng.normal(), rng.normal()])
+        lf = -np.log1p(np.exp(-u[2]))
+        if trial % 2:
+            u[1] = lf + s[2] + rng.choice([-1, 1]) * 10.0 ** rng.uniform(-9, -2)   # near the tie
+        sn = oracle.cell_step("slstm", u, w, bias, s)[0]
+        assert sn[2] == max(lf + s[2], u[1]) or abs(sn[2] - max(lf + s[2], u[1])) < 1e-14
+        # exactly one of the two rescaled gates is 1
+        ip, fp = np.exp(u[1] - sn[2]), np.exp(lf + s[2] - sn[2])
+        assert max(ip, fp) == pytest.approx(1.0, abs=1e-14)
