@@ -26,6 +26,10 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream).  Outputs are valid once the stream has completed.  Only a
  *    non-NULL report makes pararnn_newton_solve wait for the stream.
+ *  - Without a report, a call is only kernel launches on `stream` (no
+ *    allocation, no memset node, no synchronisation), so it can be captured
+ *    in a HIP graph.  Each call clears its workspace with a kernel first, so
+ *    graph replays do not see each other's look-back words.
  *  - `ws` is a device workspace of at least the queried size, 256-byte
  *    aligned, whose contents need not be initialised.  Calls that overlap in
  *    time must use distinct workspaces.
