@@ -11,6 +11,7 @@ the adjoint (reverse scan) for gradients.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass, field
 
@@ -189,6 +190,7 @@ def _problem(cell, pre, w, bias, s0, cu_seqlens=None):
     st.bias = bias.data_ptr() if (c != 0 and bias is not None) else None
     st.s0 = s0.data_ptr() if s0 is not None else None
     st.cu_seqlens, st.n_seqs = _seqlens(cu_seqlens, pre[0].device)
+    _same_device(list(pre) + [w if c != 0 else None, bias if c != 0 else None, s0], pre[0].device)
     return st, c, G, S, (B, T, D)
 
 
@@ -206,6 +208,29 @@ def newton_budget(cell, T, warm_start=False, max_iters=None) -> int:
     return k
 
 
+def _same_device(tensors, device):
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError("all tensors must be on %s (got %s)" % (device, t.device))
+
+
+def _on_device(pos, name):
+    """Run a call with the device of its argument `pos` / `name` (a tensor or a list of them) current, so
+    that the kernels launch on the device that holds the data."""
+    def deco(fn):
+        @functools.wraps(fn)
+        def wrapped(*args, **kwargs):
+            x = args[pos] if len(args) > pos else kwargs.get(name)
+            t = x[0] if isinstance(x, (list, tuple)) and len(x) else x
+            if isinstance(t, torch.Tensor) and t.is_cuda:
+                with torch.cuda.device(t.device):
+                    return fn(*args, **kwargs)
+            return fn(*args, **kwargs)
+        return wrapped
+    return deco
+
+
+@_on_device(1, "pre")
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
                  final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None,
                  picard_iters=0):
@@ -230,6 +255,7 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
         out = torch.empty((S, B, T, D), dtype=torch.float32, device=dev)
     _check_dev(out, "out", torch.float32)
     _check_dev(init_guess, "init_guess", torch.float32)
+    _same_device([out, init_guess], dev)
     if tuple(out.shape) != (S, B, T, D):
         raise ValueError("out must be [S, B, T, D]")
     if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
@@ -272,6 +298,7 @@ def scan_workspace_bytes(S, B, T, D) -> int:
     return int(load_library().pararnn_scan_workspace_bytes(S, B, T, D))
 
 
+@_on_device(0, "a")
 def linear_scan(a, b, s0=None, reverse=False, out=None, cu_seqlens=None):
     """Single-pass parallel linear recurrence.
 
@@ -298,6 +325,7 @@ def linear_scan(a, b, s0=None, reverse=False, out=None, cu_seqlens=None):
     if out is None:
         out = torch.empty(b.shape, dtype=torch.float32, device=a.device)
     _check_dev(out, "out", torch.float32)
+    _same_device([b, s0, out, cu_seqlens], a.device)
     if out.shape != b.shape:
         raise ValueError("out must have b's shape")
     cu, n_seqs = _seqlens(cu_seqlens, a.device)
@@ -316,6 +344,7 @@ def vjp_workspace_bytes(cell, pre, w=None, bias=None, s0=None, cu_seqlens=None) 
     return int(load_library().pararnn_vjp_workspace_bytes(ctypes.byref(st)))
 
 
+@_on_device(1, "pre")
 def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, want_params=True, want_s0=True,
              cu_seqlens=None):
     """Gradients at trajectory s ([S,B,T,D] float32) for upstream g = dL/dh ([B,T,D] float32).
@@ -327,6 +356,7 @@ def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, wan
     dev = pre[0].device
     _check_dev(s, "s", torch.float32)
     _check_dev(g, "g", torch.float32)
+    _same_device([s, g], dev)
     if tuple(s.shape) != (S, B, T, D) or tuple(g.shape) != (B, T, D):
         raise ValueError("s must be [S,B,T,D] and g [B,T,D]")
     d_pre = torch.empty((G, B, T, D), dtype=torch.float32, device=dev)
