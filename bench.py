@@ -15,8 +15,10 @@ automatic budget over a grid of sequence lengths.  Neither is the benchmark line
 Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
 iterations the solve ran (a linear scan counts K = 1).  roofline: the steady-state fused Newton
 iteration kernel (or the scan kernel), algorithmic bytes per element x elements / its mean
-launch duration from HIP events on the launch stream.  cpu_baseline: the fp64 CPU oracle on a
-bounded sample of channels of the same workload.
+launch duration from HIP events on the launch stream; roofline.copy_gbs is a device-to-device copy's
+bandwidth on the same GPU, for context.  cpu_baseline: the fp64 CPU oracle on a bounded sample of
+channels of the same workload (value: its Newton solve + VJP; unroll_value: its sequential unroll,
+the exact solution).
 """
 from __future__ import annotations
 
@@ -217,7 +219,8 @@ def main():
                    "tol": wl.tol, "max_iters": wl.max_iters, "iters": iters, "vjp": wl.vjp},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel_name,
-                     "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms},
+                     "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
+                     "copy_gbs": copy_gbs(torch, dev)},
     }
     if vjp_events:
         vms = float(np.mean([a.elapsed_time(b2) for a, b2 in vjp_events]))
@@ -355,6 +358,25 @@ def slstm_bench(torch, dev, args):
         torch.cuda.empty_cache()
 
 
+def copy_gbs(torch, dev, mib=1024, reps=5):
+    """Device-to-device copy bandwidth on this GPU (read + write bytes / time), for context."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def copy_bench(torch, dev, args):
     n = args.copy_mib * (1 << 20) // 4
     src = torch.randn(n, device=dev)
@@ -400,7 +422,15 @@ def cpu_baseline(wl, inp, iters, n_channels):
             oracle.vjp(prob, H, np.ascontiguousarray(inp.g[bs, :, ds].T[None]), want_lambda=False, nthreads=threads)
     sec = time.perf_counter() - t0
     n = len(pick) * wl.T
+    # the exact solution by the sequential fp64 unroll on the same sample, for context
+    t1 = time.perf_counter()
+    if wl.cell == "linear":
+        oracle.linear_scan(pre[0], pre[1], dtype=dt, nthreads=threads)
+    else:
+        oracle.unroll(prob, nthreads=threads)
+    usec = time.perf_counter() - t1
     return {"value": n * k / sec, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "unroll_value": n / usec,
             "sample": "%d of %d channels, full T=%d, %s%s; %.1f s" % (
                 len(pick), wl.B * wl.D, wl.T, "linear scan" if wl.cell == "linear" else
                 "Newton (%d iterations)" % k, " + VJP" if wl.vjp else "", sec)}
