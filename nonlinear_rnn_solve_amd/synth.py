@@ -17,7 +17,9 @@ Workloads (the five benchmark shapes of this project):
 Distributions: U ~ N(0,1); recurrent weights ~ U(-0.5, 0.5); biases
 ~ N(0, 0.1^2) (0.1 is the standard deviation); LSTM forget bias = +1.0;
 linear scan a_t = sigmoid(z), z ~ N(0,1), b_t ~ N(0,1); upstream gradient
-dL/dh ~ N(0,1) fp32.
+dL/dh ~ N(0,1) fp32.  Head-wise block GRU (head size hs): each dense
+recurrent block ~ U(-1/sqrt(hs), 1/sqrt(hs)) (torch's default recurrent
+initialisation for a hidden size of hs), other draws as for the GRU.
 """
 from __future__ import annotations
 
@@ -25,8 +27,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-GATES = {"linear": 2, "gru": 3, "lstm": 4, "slstm": 4}
-STATE = {"linear": 1, "gru": 1, "lstm": 2, "slstm": 4}
+GATES = {"linear": 2, "gru": 3, "lstm": 4, "slstm": 4, "head_gru": 3}
+STATE = {"linear": 1, "gru": 1, "lstm": 2, "slstm": 4, "head_gru": 1}
 
 
 @dataclass(frozen=True)
@@ -83,6 +85,7 @@ class Inputs:
     w: np.ndarray | None = None               # [G][D] float32
     bias: np.ndarray | None = None            # [G][D] float32
     g: np.ndarray | None = None               # [B][T][D] float32 upstream gradient (VJP)
+    head_size: int = 1                        # head_gru: channels per head; w is [3][D/hs][hs][hs]
 
     @property
     def G(self):
@@ -113,11 +116,12 @@ def _sigmoid_of_normal(rng, shape):
 
 
 def make_inputs(cell: str, B: int, T: int, D: int, dtype: str = "f32", seed: int = 0,
-                with_grad: bool = False) -> Inputs:
+                with_grad: bool = False, head_size: int | None = None) -> Inputs:
     """Draw one problem of the given shape with the benchmark distributions.
 
     Draw order: pre-activation planes in gate order, then recurrent weights
-    [G][D], then biases [G][D], then (if asked) the upstream gradient.
+    [G][D] (head_gru: [3][D/hs][hs][hs]), then biases [G][D], then (if asked) the
+    upstream gradient.
     Gate orders: gru (z, r, c); lstm (i, f, o, g); slstm (z, i, f, o); linear (a, b).
     Biases ~ N(0, 0.1^2), except the forget gate's (lstm, slstm), which is 1.
     """
@@ -132,8 +136,13 @@ def make_inputs(cell: str, B: int, T: int, D: int, dtype: str = "f32", seed: int
         pre = [a, b]
     else:
         pre = [_normal(rng, shape) for _ in range(G)]
-        w = _uniform_half(rng, (G, D))
-        if cell == "gru":
+        if cell == "head_gru":
+            assert head_size is not None and head_size >= 1 and D % head_size == 0
+            w = (_uniform_half(rng, (G, D // head_size, head_size, head_size)) *
+                 np.float32(2.0 / np.sqrt(head_size))).astype(np.float32)
+        else:
+            w = _uniform_half(rng, (G, D))
+        if cell in ("gru", "head_gru"):
             bias = (rng.standard_normal(size=(G, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
         elif cell == "slstm":
             drawn = (rng.standard_normal(size=(3, D), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
@@ -148,7 +157,7 @@ def make_inputs(cell: str, B: int, T: int, D: int, dtype: str = "f32", seed: int
     if dtype == "bf16":
         pre = [f32_to_bf16_bits(p) for p in pre]
     g = _normal(rng, shape) if with_grad else None
-    return Inputs(cell, B, T, D, dtype, pre, w, bias, g)
+    return Inputs(cell, B, T, D, dtype, pre, w, bias, g, head_size if cell == "head_gru" else 1)
 
 
 def workload_inputs(wl: Workload, seed: int | None = None, B=None, T=None, D=None) -> Inputs:

@@ -1,7 +1,8 @@
 """CPU oracle for the ParaRNN hot path -- TEST INFRASTRUCTURE ONLY.
 
 A plain fp64 implementation (``pararnn_oracle.c``) of what the GPU library
-computes: the sequential unroll of a diagonal GRU / LSTM / sLSTM / linear cell, Newton
+computes: the sequential unroll of a diagonal GRU / LSTM / sLSTM / linear cell or of the
+head-wise block GRU (dense recurrent block per head), Newton
 on F(H)_t = h_t - f(h_{t-1}, x_t) = 0 with a *sequential* linear solve, the
 linear recurrence itself (forward and reverse, state size 1 or 2), and the
 adjoint (VJP) at a solved trajectory.  Sources: pararnn-torch README (PyPI
@@ -27,18 +28,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pararnn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-LINEAR, GRU, LSTM, SLSTM = 0, 1, 2, 3
+LINEAR, GRU, LSTM, SLSTM, HEAD_GRU = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-CELLS = {"linear": LINEAR, "gru": GRU, "lstm": LSTM, "slstm": SLSTM}
+CELLS = {"linear": LINEAR, "gru": GRU, "lstm": LSTM, "slstm": SLSTM, "head_gru": HEAD_GRU}
 OK, EINVAL, ENOMEM, DIVERGED = 0, -1, -2, -5
 
 
 def state_size(cell: int) -> int:
-    return {LINEAR: 1, GRU: 1, LSTM: 2, SLSTM: 4}[cell]
+    return {LINEAR: 1, GRU: 1, LSTM: 2, SLSTM: 4, HEAD_GRU: 1}[cell]
 
 
 def gate_count(cell: int) -> int:
-    return {LINEAR: 2, GRU: 3, LSTM: 4, SLSTM: 4}[cell]
+    return {LINEAR: 2, GRU: 3, LSTM: 4, SLSTM: 4, HEAD_GRU: 3}[cell]
 
 
 def build(force: bool = False) -> str:
@@ -66,7 +67,8 @@ def _load():
         lib.or_newton.argtypes = [vp, vp, i32, i32, i32, dbl, vp, vp, vp, vp, i32]
         lib.or_linear_scan.argtypes = [i32, i64, i64, i64, i32, vp, vp, vp, vp, i32, vp, i32]
         lib.or_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        assert lib.or_abi_version() == 6
+        lib.or_hgru_step.argtypes = [i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        assert lib.or_abi_version() == 7
         _lib = lib
     return _lib
 
@@ -75,7 +77,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("cell", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("pre", ctypes.c_void_p * 4), ("w", ctypes.c_void_p),
-                ("bias", ctypes.c_void_p), ("s0", ctypes.c_void_p), ("seg_start", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("s0", ctypes.c_void_p), ("seg_start", ctypes.c_void_p),
+                ("head_size", ctypes.c_int64)]
 
 
 def default_threads() -> int:
@@ -107,7 +110,8 @@ def _as_pre(pre, dtype):
 class Problem:
     """Holds contiguous copies of the inputs and the ctypes struct that points at them."""
 
-    def __init__(self, cell, pre, w=None, bias=None, s0=None, dtype=F32, cu_seqlens=None):
+    def __init__(self, cell, pre, w=None, bias=None, s0=None, dtype=F32, cu_seqlens=None, head_size=None):
+        """head_gru: w is [3][n_heads][hs][hs] (block row = output channel) and head_size = hs."""
         cell = CELLS.get(cell, cell)
         self.cell, self.dtype = cell, dtype
         self.pre = _as_pre(pre, dtype)
@@ -118,7 +122,12 @@ class Problem:
             assert p.shape == (B, T, D)
         self.B, self.T, self.D = B, T, D
         self.S = state_size(cell)
-        self.w = None if w is None else np.ascontiguousarray(w, dtype=np.float32).reshape(G, D)
+        self.head_size = 1
+        if cell == HEAD_GRU:
+            assert head_size is not None and head_size >= 1 and D % head_size == 0
+            self.head_size = int(head_size)
+        wcols = D * self.head_size
+        self.w = None if w is None else np.ascontiguousarray(w, dtype=np.float32).reshape(G, wcols)
         self.bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32).reshape(G, D)
         if cell != LINEAR:
             assert self.w is not None and self.bias is not None
@@ -130,6 +139,7 @@ class Problem:
         st.w, st.bias, st.s0 = _ptr(self.w), _ptr(self.bias), _ptr(self.s0)
         self.seg_start = seg_start_flags(cu_seqlens, T)
         st.seg_start = _ptr(self.seg_start)
+        st.head_size = self.head_size
         self.struct = st
 
     def traj_shape(self):
@@ -155,6 +165,21 @@ def cell_step(cell, u, w, bias, s):
     _check(_load().or_cell_step(cell, _ptr(u), _ptr(w), _ptr(bias), _ptr(s), _ptr(sn),
                                 _ptr(J), _ptr(dfdu), _ptr(wc)), "cell_step")
     return sn, J.reshape(S, S), dfdu.reshape(S, G), wc
+
+
+def hgru_step(u, A, bias, h):
+    """One step of one head of the head-wise block GRU in fp64.  u [3][hs], A [3][hs][hs],
+    bias [3][hs], h [hs].  Returns (h_next, J [hs][hs], dz [hs], dc [hs], dr [hs][hs], rh [hs])."""
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    hs = A.shape[-1]
+    u = np.ascontiguousarray(u, dtype=np.float64).reshape(3 * hs)
+    bias = np.ascontiguousarray(bias, dtype=np.float64).reshape(3 * hs)
+    h = np.ascontiguousarray(h, dtype=np.float64).reshape(hs)
+    hn, dz, dc, rh = np.zeros(hs), np.zeros(hs), np.zeros(hs), np.zeros(hs)
+    J, dr = np.zeros(hs * hs), np.zeros(hs * hs)
+    _check(_load().or_hgru_step(hs, _ptr(u), _ptr(A), _ptr(bias), _ptr(h), _ptr(hn), _ptr(J), _ptr(dz), _ptr(dc),
+                                _ptr(dr), _ptr(rh)), "hgru_step")
+    return hn, J.reshape(hs, hs), dz, dc, dr.reshape(hs, hs), rh
 
 
 def unroll(prob: Problem, nthreads=None):
@@ -209,13 +234,19 @@ def linear_scan(a, b, s0=None, reverse=False, S=1, dtype=F32, nthreads=None, cu_
 def vjp(prob: Problem, s, g, want_lambda=True, nthreads=None):
     """Adjoint at trajectory s ([S][B][T][D]); g = dL/dh [B][T][D].
 
-    Returns dict with d_pre [G][B][T][D], d_w [G][D], d_bias [G][D], d_s0 [S][B][D], lam [S][B][T][D].
+    Returns dict with d_pre [G][B][T][D], d_w [G][D] (head_gru: [3][n_heads][hs][hs]), d_bias [G][D],
+    d_s0 [S][B][D], lam [S][B][T][D].
     """
     G = gate_count(prob.cell)
     s = np.ascontiguousarray(s, dtype=np.float64).reshape(prob.traj_shape())
     g = np.ascontiguousarray(g, dtype=np.float32).reshape(prob.B, prob.T, prob.D)
     d_pre = np.zeros((G, prob.B, prob.T, prob.D))
-    d_w, d_bias = np.zeros((G, prob.D)), np.zeros((G, prob.D))
+    if prob.cell == HEAD_GRU:
+        hs = prob.head_size
+        d_w = np.zeros((G, prob.D // hs, hs, hs))
+    else:
+        d_w = np.zeros((G, prob.D))
+    d_bias = np.zeros((G, prob.D))
     d_s0 = np.zeros((prob.S, prob.B, prob.D))
     lam = np.zeros(prob.traj_shape()) if want_lambda else None
     _check(_load().or_vjp(ctypes.byref(prob.struct), _ptr(s), _ptr(g), _ptr(d_pre), _ptr(d_w), _ptr(d_bias),

@@ -34,7 +34,7 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1 };
-enum { OR_LINEAR = 0, OR_GRU = 1, OR_LSTM = 2, OR_SLSTM = 3 };
+enum { OR_LINEAR = 0, OR_GRU = 1, OR_LSTM = 2, OR_SLSTM = 3, OR_HGRU = 4 };
 /* largest state size and gate count of the cells below */
 enum { OR_SMAX = 4, OR_GMAX = 4 };
 enum { OR_OK = 0, OR_EINVAL = -1, OR_ENOMEM = -2, OR_DIVERGED = -5 };
@@ -60,7 +60,7 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 static int state_size(int cell) { return cell == OR_SLSTM ? 4 : (cell == OR_LSTM ? 2 : 1); }
 static int gate_count(int cell) {
-  return (cell == OR_LSTM || cell == OR_SLSTM) ? 4 : (cell == OR_GRU ? 3 : 2);
+  return (cell == OR_LSTM || cell == OR_SLSTM) ? 4 : ((cell == OR_GRU || cell == OR_HGRU) ? 3 : 2);
 }
 
 /* log(sigmoid(x)) without overflow for either sign of x */
@@ -226,6 +226,8 @@ typedef struct {
   const unsigned char* seg_start; /* [T] or NULL: nonzero where a new packed sequence begins
                                      (that step's previous state is zero; s0 is the first
                                      sequence's initial state)                              */
+  int64_t head_size;   /* OR_HGRU: channels per head (D = n_heads * head_size); w is then
+                          [3][n_heads][head_size][head_size]; ignored by the other cells    */
 } or_problem;
 
 static int64_t elem_index(const or_problem* p, int64_t b, int64_t t, int64_t d) {
@@ -271,6 +273,15 @@ static void prev_state(const or_problem* p, const double* H, int64_t b, int64_t 
   else for (int k = 0; k < S; ++k) prev[k] = H[traj_index(p, k, b, t - 1, d)];
 }
 
+/* head-wise block GRU entry points (defined at the end of this file) */
+static int hgru_unroll(const or_problem* p, double* out, int nthreads);
+static int hgru_residual(const or_problem* p, const double* H, double* out_max, int nthreads);
+static int hgru_newton(const or_problem* p, double* H, int picard_iters, int max_iters, double tol,
+                       double* resid, int* iters, int* converged, int nthreads);
+static int hgru_warm(const or_problem* p, double* H, int nthreads);
+static int hgru_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, double* d_w,
+                    double* d_bias, double* d_s0, double* lam, int nthreads);
+
 /* ------------------------------------------------------------------------ */
 /* a tiny thread pool over channels                                          */
 /* ------------------------------------------------------------------------ */
@@ -313,7 +324,9 @@ static int run_channels(int64_t n_channels, int nthreads, channel_fn fn, void* c
 
 static int check_problem(const or_problem* p) {
   if (!p || p->B < 0 || p->T < 0 || p->D < 0) return OR_EINVAL;
-  if (p->cell != OR_LINEAR && p->cell != OR_GRU && p->cell != OR_LSTM && p->cell != OR_SLSTM) return OR_EINVAL;
+  if (p->cell != OR_LINEAR && p->cell != OR_GRU && p->cell != OR_LSTM && p->cell != OR_SLSTM &&
+      p->cell != OR_HGRU) return OR_EINVAL;
+  if (p->cell == OR_HGRU && (p->head_size < 1 || p->D % p->head_size != 0)) return OR_EINVAL;
   if (p->dtype != OR_F32 && p->dtype != OR_BF16) return OR_EINVAL;
   int G = gate_count(p->cell);
   for (int g = 0; g < G; ++g)
@@ -356,6 +369,7 @@ static void unroll_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
 int or_unroll(const or_problem* p, double* out, int nthreads) {
   int rc = check_problem(p);
   if (rc) return rc;
+  if (p->cell == OR_HGRU) return hgru_unroll(p, out, nthreads);
   unroll_ctx c = {p, out};
   return run_channels(p->B * p->D, nthreads, unroll_channels, &c);
 }
@@ -394,6 +408,7 @@ static void resid_channels(void* vctx, int64_t ch0, int64_t ch1, int worker) {
 int or_residual(const or_problem* p, const double* H, double* out_max, int nthreads) {
   int rc = check_problem(p);
   if (rc) return rc;
+  if (p->cell == OR_HGRU) return hgru_residual(p, H, out_max, nthreads);
   if (nthreads < 1) nthreads = 1;
   double* wm = (double*)calloc((size_t)nthreads, sizeof(double));
   if (!wm) return OR_ENOMEM;
@@ -511,6 +526,13 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int p
   int64_t n = (int64_t)S * p->B * p->T * p->D;
   for (int64_t i = 0; i < n; ++i) H[i] = init_guess ? (double)init_guess[i] : 0.0;
   if (nthreads < 1) nthreads = 1;
+  if (p->cell == OR_HGRU) {
+    if (!init_guess && init_mode == 1) {
+      rc = hgru_warm(p, H, nthreads);
+      if (rc) return rc;
+    }
+    return hgru_newton(p, H, picard_iters, max_iters, tol, resid, iters, converged, nthreads);
+  }
   if (!init_guess && init_mode == 1) {
     warm_ctx wc = {p, H};
     rc = run_channels(p->B * p->D, nthreads, warm_channels, &wc);
@@ -699,6 +721,7 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
            double* d_bias, double* d_s0, double* lam, int nthreads) {
   int rc = check_problem(p);
   if (rc) return rc;
+  if (p->cell == OR_HGRU) return hgru_vjp(p, s, g, d_pre, d_w, d_bias, d_s0, lam, nthreads);
   int S = state_size(p->cell), G = gate_count(p->cell);
   int64_t C = p->B * p->D;
   if (nthreads < 1) nthreads = 1;
@@ -729,5 +752,404 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
   return rc;
 }
 
+/* ------------------------------------------------------------------------ */
+/* head-wise block GRU                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * pararnn-torch README, "Usage" (Dreamer-style block GRU: ParaGRU with
+ * mix="head" and n_heads; block-diagonal A_*, factorized Newton) and "News"
+ * (factorized Newton for that cell).  The page prints no equations.  Reading:
+ * the channels split into n_heads heads of hs = D / n_heads consecutive
+ * channels; each gate's recurrent matrix A_g is block-diagonal with one dense
+ * hs x hs block per head, and otherwise the cell is the diagonal GRU above
+ * with A_g in place of the diagonal weight (A_c acts on r * h):
+ *   z = sig(U_z + A_z h + b_z),  r = sig(U_r + A_r h + b_r),
+ *   c = tanh(U_c + A_c (r * h) + b_c),  h' = (1 - z) * h + z * c
+ * (hs = 1 is the diagonal GRU).  Heads do not interact, so F(H) = 0 and its
+ * Newton system split into one block-bidiagonal system per (batch row, head)
+ * with dense hs x hs Jacobian blocks: that split is read as the
+ * "factorization".  Newton uses the exact block Jacobian.
+ * Layout: w = [3][n_heads][hs][hs], block row i = output channel, column j =
+ * input channel; bias = [3][D]; gate order z, r, c.
+ */
+
+static int64_t hgru_heads(const or_problem* p) { return p->D / p->head_size; }
+
+/* One step of one head in fp64.  u = 3*hs gate inputs, A = [3][hs][hs], bias = 3*hs, h = hs.
+   Outputs: hn[hs]; optional J[hs*hs] (J[i*hs+j] = d hn_i / d h_j), dz[hs] = d hn_i / d u_z,i,
+   dc[hs] = d hn_i / d u_c,i, dr[hs*hs] (dr[i*hs+k] = d hn_i / d u_r,k), rh[hs] = r_j h_j (the
+   vector A_c multiplies).  Caller-provided work space: none (hs <= OR_HMAX). */
+enum { OR_HMAX = 256 };
+int or_hgru_step(int64_t hs, const double* u, const double* A, const double* bias, const double* h,
+                 double* hn, double* J, double* dz, double* dc, double* dr, double* rh) {
+  if (hs < 1 || hs > OR_HMAX) return OR_EINVAL;
+  const double *Az = A, *Ar = A + hs * hs, *Ac = A + 2 * hs * hs;
+  double z[OR_HMAX], r[OR_HMAX], c[OR_HMAX], rv[OR_HMAX], pz[OR_HMAX], pc[OR_HMAX];
+  for (int64_t i = 0; i < hs; ++i) {
+    double az = 0.0, ar = 0.0;
+    for (int64_t j = 0; j < hs; ++j) {
+      az += Az[i * hs + j] * h[j];
+      ar += Ar[i * hs + j] * h[j];
+    }
+    z[i] = sigmoid(u[i] + az + bias[i]);
+    r[i] = sigmoid(u[hs + i] + ar + bias[hs + i]);
+  }
+  for (int64_t j = 0; j < hs; ++j) rv[j] = r[j] * h[j];
+  for (int64_t i = 0; i < hs; ++i) {
+    double ac = 0.0;
+    for (int64_t j = 0; j < hs; ++j) ac += Ac[i * hs + j] * rv[j];
+    c[i] = tanh(u[2 * hs + i] + ac + bias[2 * hs + i]);
+    hn[i] = (1.0 - z[i]) * h[i] + z[i] * c[i];
+    pz[i] = (c[i] - h[i]) * z[i] * (1.0 - z[i]);   /* via z_i            */
+    pc[i] = z[i] * (1.0 - c[i] * c[i]);            /* via c_i            */
+  }
+  if (dz) for (int64_t i = 0; i < hs; ++i) dz[i] = pz[i];
+  if (dc) for (int64_t i = 0; i < hs; ++i) dc[i] = pc[i];
+  if (rh) for (int64_t j = 0; j < hs; ++j) rh[j] = rv[j];
+  /* u_r,k moves h'_i through c_i: d u_c,i / d u_r,k = A_c[i][k] h_k r_k (1 - r_k) */
+  if (dr)
+    for (int64_t i = 0; i < hs; ++i)
+      for (int64_t k = 0; k < hs; ++k) dr[i * hs + k] = pc[i] * Ac[i * hs + k] * h[k] * r[k] * (1.0 - r[k]);
+  if (J) {
+    /* d h'_i / d h_j = (1 - z_i) [i = j] + (c_i - h_i) z_i (1 - z_i) A_z[i][j]
+                        + z_i (1 - c_i^2) d u_c,i / d h_j,
+       d u_c,i / d h_j = A_c[i][j] r_j + sum_k A_c[i][k] h_k r_k (1 - r_k) A_r[k][j] */
+    for (int64_t i = 0; i < hs; ++i) {
+      for (int64_t j = 0; j < hs; ++j) {
+        double duc = Ac[i * hs + j] * r[j];
+        for (int64_t k = 0; k < hs; ++k) duc += Ac[i * hs + k] * h[k] * r[k] * (1.0 - r[k]) * Ar[k * hs + j];
+        J[i * hs + j] = (i == j ? 1.0 - z[i] : 0.0) + pz[i] * Az[i * hs + j] + pc[i] * duc;
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* a chain is one (batch row, head): ch = b * n_heads + head */
+static void hgru_params(const or_problem* p, int64_t head, double* A, double* bias) {
+  const int64_t hs = p->head_size, H = hgru_heads(p);
+  for (int g = 0; g < 3; ++g) {
+    for (int64_t i = 0; i < hs * hs; ++i) A[g * hs * hs + i] = (double)p->w[(g * H + head) * hs * hs + i];
+    for (int64_t i = 0; i < hs; ++i) bias[g * hs + i] = (double)p->bias[g * p->D + head * hs + i];
+  }
+}
+
+static void hgru_gather(const or_problem* p, int64_t b, int64_t t, int64_t head, double* u) {
+  const int64_t hs = p->head_size;
+  for (int g = 0; g < 3; ++g)
+    for (int64_t i = 0; i < hs; ++i) u[g * hs + i] = load_in(p->pre[g], p->dtype, elem_index(p, b, t, head * hs + i));
+}
+
+/* the state step t of chain (b, head) starts from: s0, zero at a sequence start, else H_{t-1} */
+static void hgru_prev(const or_problem* p, const double* H, int64_t b, int64_t t, int64_t head, double* prev) {
+  const int64_t hs = p->head_size;
+  for (int64_t i = 0; i < hs; ++i) {
+    const int64_t d = head * hs + i;
+    if (t == 0) prev[i] = p->s0 ? (double)p->s0[b * p->D + d] : 0.0;
+    else if (starts_at(p, t)) prev[i] = 0.0;
+    else prev[i] = H[elem_index(p, b, t - 1, d)];
+  }
+}
+
+/* per-worker buffers of one chain walk */
+typedef struct {
+  double *A, *bias, *u, *prev, *hn, *J, *dz, *dc, *dr, *rh, *old, *delta, *lam, *tmp;
+} hgru_buf;
+
+static int hgru_buf_alloc(hgru_buf* w, int64_t hs, int64_t T, int want_lam) {
+  const size_t v = (size_t)hs, m = (size_t)(hs * hs);
+  double* base = (double*)malloc(sizeof(double) * (3 * m + 3 * v + 3 * v + 10 * v + 2 * m +
+                                                   (want_lam ? (size_t)(T > 0 ? T : 1) * v : 0)));
+  if (!base) return OR_ENOMEM;
+  double* q = base;
+  w->A = q; q += 3 * m;
+  w->bias = q; q += 3 * v;
+  w->u = q; q += 3 * v;
+  w->prev = q; q += v;
+  w->hn = q; q += v;
+  w->dz = q; q += v;
+  w->dc = q; q += v;
+  w->rh = q; q += v;
+  w->old = q; q += v;
+  w->delta = q; q += v;
+  w->tmp = q; q += 3 * v;
+  w->J = q; q += m;
+  w->dr = q; q += m;
+  w->lam = want_lam ? q : NULL;
+  return OR_OK;
+}
+
+typedef struct {
+  const or_problem* p;
+  double* H;           /* trajectory [B][T][D] (in/out where it applies) */
+  const double* Hc;    /* read-only trajectory */
+  double* worker_max;
+  int picard;
+  int status;
+} hgru_ctx;
+
+static void hgru_unroll_chains(void* vctx, int64_t c0, int64_t c1, int worker) {
+  (void)worker;
+  hgru_ctx* c = (hgru_ctx*)vctx;
+  const or_problem* p = c->p;
+  const int64_t hs = p->head_size, H = hgru_heads(p);
+  hgru_buf w;
+  if (hgru_buf_alloc(&w, hs, p->T, 0)) { c->status = OR_ENOMEM; return; }
+  for (int64_t ch = c0; ch < c1; ++ch) {
+    const int64_t b = ch / H, head = ch % H;
+    hgru_params(p, head, w.A, w.bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      hgru_prev(p, c->H, b, t, head, w.prev);
+      hgru_gather(p, b, t, head, w.u);
+      or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, NULL, NULL, NULL, NULL, NULL);
+      for (int64_t i = 0; i < hs; ++i) c->H[elem_index(p, b, t, head * hs + i)] = w.hn[i];
+    }
+  }
+  free(w.A);
+}
+
+static int hgru_unroll(const or_problem* p, double* out, int nthreads) {
+  hgru_ctx c = {p, out, NULL, NULL, 0, OR_OK};
+  int rc = run_channels(p->B * hgru_heads(p), nthreads, hgru_unroll_chains, &c);
+  return rc ? rc : c.status;
+}
+
+static void hgru_resid_chains(void* vctx, int64_t c0, int64_t c1, int worker) {
+  hgru_ctx* c = (hgru_ctx*)vctx;
+  const or_problem* p = c->p;
+  const int64_t hs = p->head_size, H = hgru_heads(p);
+  hgru_buf w;
+  if (hgru_buf_alloc(&w, hs, p->T, 0)) { c->status = OR_ENOMEM; return; }
+  double m = 0.0;
+  for (int64_t ch = c0; ch < c1; ++ch) {
+    const int64_t b = ch / H, head = ch % H;
+    hgru_params(p, head, w.A, w.bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      hgru_prev(p, c->Hc, b, t, head, w.prev);
+      hgru_gather(p, b, t, head, w.u);
+      or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, NULL, NULL, NULL, NULL, NULL);
+      for (int64_t i = 0; i < hs; ++i) m = nan_max(m, fabs(c->Hc[elem_index(p, b, t, head * hs + i)] - w.hn[i]));
+    }
+  }
+  c->worker_max[worker] = m;
+  free(w.A);
+}
+
+static int hgru_residual(const or_problem* p, const double* Hv, double* out_max, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  double* wm = (double*)calloc((size_t)nthreads, sizeof(double));
+  if (!wm) return OR_ENOMEM;
+  hgru_ctx c = {p, NULL, Hv, wm, 0, OR_OK};
+  int rc = run_channels(p->B * hgru_heads(p), nthreads, hgru_resid_chains, &c);
+  double m = 0.0;
+  for (int i = 0; i < nthreads; ++i) m = nan_max(m, wm[i]);
+  free(wm);
+  *out_max = m;
+  return rc ? rc : c.status;
+}
+
+/* Newton iteration k on each chain, as in or_newton: r_t = h^k_t - f(h^k_{t-1}, x_t), J_t the
+   dense hs x hs block, delta_{-1} = 0, delta_t = J_t delta_{t-1} - r_t (solved sequentially),
+   H^{k+1} = H^k + delta.  The walk goes forward in t and keeps the old h^k_{t-1} aside, so the
+   residual and Jacobian of every step are taken at the old iterate. */
+static void hgru_newton_chains(void* vctx, int64_t c0, int64_t c1, int worker) {
+  hgru_ctx* c = (hgru_ctx*)vctx;
+  const or_problem* p = c->p;
+  const int64_t hs = p->head_size, H = hgru_heads(p);
+  hgru_buf w;
+  if (hgru_buf_alloc(&w, hs, p->T, 0)) { c->status = OR_ENOMEM; return; }
+  double m = 0.0;
+  for (int64_t ch = c0; ch < c1; ++ch) {
+    const int64_t b = ch / H, head = ch % H;
+    hgru_params(p, head, w.A, w.bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      /* the previous state at the OLD iterate: s0, zero at a sequence start, else old h_{t-1} */
+      if (t == 0 || starts_at(p, t)) hgru_prev(p, c->H, b, t, head, w.prev);
+      else for (int64_t i = 0; i < hs; ++i) w.prev[i] = w.old[i];
+      hgru_gather(p, b, t, head, w.u);
+      or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, w.J, NULL, NULL, NULL, NULL);
+      const int no_jac = c->picard || starts_at(p, t);   /* as in or_newton: J = 0 there */
+      for (int64_t i = 0; i < hs; ++i) {
+        const int64_t e = elem_index(p, b, t, head * hs + i);
+        const double r = c->H[e] - w.hn[i];
+        m = nan_max(m, fabs(r));
+        double acc = -r;
+        if (t > 0 && !no_jac)
+          for (int64_t j = 0; j < hs; ++j) acc += w.J[i * hs + j] * w.delta[j];
+        w.tmp[i] = acc;
+      }
+      for (int64_t i = 0; i < hs; ++i) {
+        const int64_t e = elem_index(p, b, t, head * hs + i);
+        w.old[i] = c->H[e];
+        w.delta[i] = w.tmp[i];
+        c->H[e] += w.delta[i];
+      }
+    }
+  }
+  c->worker_max[worker] = m;
+  free(w.A);
+}
+
+static int hgru_newton(const or_problem* p, double* Hv, int picard_iters, int max_iters, double tol,
+                       double* resid, int* iters, int* converged, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  double* wm = (double*)malloc(sizeof(double) * (size_t)nthreads);
+  if (!wm) return OR_ENOMEM;
+  hgru_ctx c = {p, Hv, NULL, wm, 0, OR_OK};
+  int k_done = 0, conv = 0, status = OR_OK;
+  for (int k = 0; k < max_iters; ++k) {
+    c.picard = k < picard_iters;
+    for (int i = 0; i < nthreads; ++i) wm[i] = 0.0;
+    int rc = run_channels(p->B * hgru_heads(p), nthreads, hgru_newton_chains, &c);
+    if (rc || c.status) { status = rc ? rc : c.status; break; }
+    double R = 0.0;
+    for (int i = 0; i < nthreads; ++i) R = nan_max(R, wm[i]);
+    resid[k] = R;
+    k_done = k + 1;
+    if (!isfinite(R)) { status = OR_DIVERGED; break; }
+    if (tol > 0.0 && R < tol) { conv = 1; break; }
+  }
+  free(wm);
+  *iters = k_done;
+  *converged = conv;
+  return status;
+}
+
+/* warm start: H^0_t = f(0, x_t) */
+static void hgru_warm_chains(void* vctx, int64_t c0, int64_t c1, int worker) {
+  (void)worker;
+  hgru_ctx* c = (hgru_ctx*)vctx;
+  const or_problem* p = c->p;
+  const int64_t hs = p->head_size, H = hgru_heads(p);
+  hgru_buf w;
+  if (hgru_buf_alloc(&w, hs, p->T, 0)) { c->status = OR_ENOMEM; return; }
+  for (int64_t i = 0; i < hs; ++i) w.prev[i] = 0.0;
+  for (int64_t ch = c0; ch < c1; ++ch) {
+    const int64_t b = ch / H, head = ch % H;
+    hgru_params(p, head, w.A, w.bias);
+    for (int64_t t = 0; t < p->T; ++t) {
+      hgru_gather(p, b, t, head, w.u);
+      or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, NULL, NULL, NULL, NULL, NULL);
+      for (int64_t i = 0; i < hs; ++i) c->H[elem_index(p, b, t, head * hs + i)] = w.hn[i];
+    }
+  }
+  free(w.A);
+}
+
+static int hgru_warm(const or_problem* p, double* Hv, int nthreads) {
+  hgru_ctx c = {p, Hv, NULL, NULL, 0, OR_OK};
+  int rc = run_channels(p->B * hgru_heads(p), nthreads, hgru_warm_chains, &c);
+  return rc ? rc : c.status;
+}
+
+/* VJP, as or_vjp with dense blocks: lambda_{T-1} = g_{T-1}, lambda_t = g_t + J_{t+1}^T lambda_{t+1}
+   (zero across a sequence start); then per step
+     dU_z,i = lambda_i dz_i,  dU_c,i = lambda_i dc_i,  dU_r,k = sum_i lambda_i dr[i][k],
+     dA_z[i][j] += dU_z,i h_j,  dA_r[i][j] += dU_r,i h_j,  dA_c[i][j] += dU_c,i (r h)_j,
+     dbias_g,i += dU_g,i     (h = the step's previous state),
+   dL/ds0 = J_0^T lambda_0.  Sums: per chain in t order, then over b ascending per head. */
+typedef struct {
+  const or_problem* p;
+  const double* s;
+  const float* g;
+  double* d_pre;     /* [3][B][T][D] */
+  double* lam;       /* [B][T][D] or NULL */
+  double* d_s0;      /* [B][D] or NULL */
+  double* apart;     /* [B*H][3][hs][hs] */
+  double* bpart;     /* [B*H][3][hs] */
+  int status;
+} hgru_vjp_ctx;
+
+static void hgru_vjp_chains(void* vctx, int64_t c0, int64_t c1, int worker) {
+  (void)worker;
+  hgru_vjp_ctx* c = (hgru_vjp_ctx*)vctx;
+  const or_problem* p = c->p;
+  const int64_t hs = p->head_size, H = hgru_heads(p), T = p->T, N = p->B * p->T * p->D;
+  hgru_buf w;
+  if (hgru_buf_alloc(&w, hs, T, 1)) { c->status = OR_ENOMEM; return; }
+  for (int64_t ch = c0; ch < c1; ++ch) {
+    const int64_t b = ch / H, head = ch % H;
+    hgru_params(p, head, w.A, w.bias);
+    for (int64_t t = T - 1; t >= 0; --t) {
+      for (int64_t i = 0; i < hs; ++i) w.tmp[i] = (double)c->g[elem_index(p, b, t, head * hs + i)];
+      if (t + 1 < T && !starts_at(p, t + 1)) {
+        for (int64_t i = 0; i < hs; ++i) w.prev[i] = c->s[elem_index(p, b, t, head * hs + i)];
+        hgru_gather(p, b, t + 1, head, w.u);
+        or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, w.J, NULL, NULL, NULL, NULL);
+        for (int64_t i = 0; i < hs; ++i)        /* (J^T lambda)_i = sum_j J[j][i] lambda_j */
+          for (int64_t j = 0; j < hs; ++j) w.tmp[i] += w.J[j * hs + i] * w.lam[(t + 1) * hs + j];
+      }
+      for (int64_t i = 0; i < hs; ++i) w.lam[t * hs + i] = w.tmp[i];
+    }
+    double* ap = c->apart + ch * 3 * hs * hs;
+    double* bp = c->bpart + ch * 3 * hs;
+    for (int64_t i = 0; i < 3 * hs * hs; ++i) ap[i] = 0.0;
+    for (int64_t i = 0; i < 3 * hs; ++i) bp[i] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      hgru_prev(p, c->s, b, t, head, w.prev);
+      hgru_gather(p, b, t, head, w.u);
+      or_hgru_step(hs, w.u, w.A, w.bias, w.prev, w.hn, w.J, w.dz, w.dc, w.dr, w.rh);
+      const double* lam = w.lam + t * hs;
+      double* du = w.tmp;   /* du[g*hs + i] */
+      for (int64_t i = 0; i < hs; ++i) {
+        du[i] = lam[i] * w.dz[i];
+        du[2 * hs + i] = lam[i] * w.dc[i];
+        double acc = 0.0;
+        for (int64_t k = 0; k < hs; ++k) acc += lam[k] * w.dr[k * hs + i];
+        du[hs + i] = acc;
+      }
+      for (int g = 0; g < 3; ++g) {
+        const double* x = (g == 2) ? w.rh : w.prev;   /* the vector A_g multiplies */
+        for (int64_t i = 0; i < hs; ++i) {
+          const int64_t e = elem_index(p, b, t, head * hs + i);
+          c->d_pre[g * N + e] = du[g * hs + i];
+          bp[g * hs + i] += du[g * hs + i];
+          for (int64_t j = 0; j < hs; ++j) ap[(g * hs + i) * hs + j] += du[g * hs + i] * x[j];
+        }
+      }
+      if (c->lam)
+        for (int64_t i = 0; i < hs; ++i) c->lam[elem_index(p, b, t, head * hs + i)] = lam[i];
+      if (t == 0 && c->d_s0)
+        for (int64_t i = 0; i < hs; ++i) {
+          double acc = 0.0;
+          for (int64_t j = 0; j < hs; ++j) acc += w.J[j * hs + i] * lam[j];
+          c->d_s0[b * p->D + head * hs + i] = acc;
+        }
+    }
+    if (T == 0 && c->d_s0)
+      for (int64_t i = 0; i < hs; ++i) c->d_s0[b * p->D + head * hs + i] = 0.0;
+  }
+  free(w.A);
+}
+
+static int hgru_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, double* d_w,
+                    double* d_bias, double* d_s0, double* lam, int nthreads) {
+  const int64_t hs = p->head_size, H = hgru_heads(p), C = p->B * H;
+  double* apart = (double*)calloc((size_t)(C > 0 ? C : 1) * 3 * (size_t)(hs * hs), sizeof(double));
+  double* bpart = (double*)calloc((size_t)(C > 0 ? C : 1) * 3 * (size_t)hs, sizeof(double));
+  if (!apart || !bpart) { free(apart); free(bpart); return OR_ENOMEM; }
+  hgru_vjp_ctx c = {p, s, g, d_pre, lam, d_s0, apart, bpart, OR_OK};
+  int rc = run_channels(C, nthreads, hgru_vjp_chains, &c);
+  if (!rc) rc = c.status;
+  if (rc == OR_OK) {
+    for (int gi = 0; gi < 3; ++gi)
+      for (int64_t head = 0; head < H; ++head) {
+        for (int64_t e = 0; e < hs * hs; ++e) {
+          double acc = 0.0;
+          for (int64_t b = 0; b < p->B; ++b) acc += apart[((b * H + head) * 3 + gi) * hs * hs + e];
+          if (d_w) d_w[(gi * H + head) * hs * hs + e] = acc;
+        }
+        for (int64_t i = 0; i < hs; ++i) {
+          double acc = 0.0;
+          for (int64_t b = 0; b < p->B; ++b) acc += bpart[((b * H + head) * 3 + gi) * hs + i];
+          if (d_bias) d_bias[gi * p->D + head * hs + i] = acc;
+        }
+      }
+  }
+  free(apart);
+  free(bpart);
+  return rc;
+}
+
 /* ABI version of this file's entry points, so the wrapper can check it */
-int or_abi_version(void) { return 6; }
+int or_abi_version(void) { return 7; }
