@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PARARNN_ABI_VERSION 4
+#define PARARNN_ABI_VERSION 5
 /* upper bound of Newton iterations per call (report.residual holds one more) */
 #define PARARNN_MAX_ITERS 64
 
@@ -77,9 +77,19 @@ typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
  *              m' = max(lf + m, u_i),  i' = exp(u_i - m'),  f' = exp(lf + m - m'),
  *              c' = f' c + i' z,  n' = f' n + i',  h' = o c' / n'
  *             (at a tie of the max the forget branch is taken).  Its Newton iteration wants a few
- *             Picard sweeps first (opts.picard_iters); it has no measured budget (max_iters > 0). */
+ *             Picard sweeps first (opts.picard_iters); it has no measured budget (max_iters > 0).
+ *  HEAD_GRU  G=3 (z, r, c), S=1: the head-wise block GRU of the pararnn-torch README ("Usage":
+ *             ParaGRU with mix="head" and n_heads, block-diagonal A_*, factorized Newton).  The D
+ *             channels form D / head_size heads of head_size consecutive channels; each gate's
+ *             recurrent matrix is block-diagonal with one dense head_size x head_size block per head:
+ *              z = sig(U_z + A_z h + b_z),  r = sig(U_r + A_r h + b_r),
+ *              c = tanh(U_c + A_c (r h) + b_c),  h' = (1 - z) h + z c
+ *             w is [3][D / head_size][head_size][head_size] (block row = output channel, column =
+ *             input channel), bias [3][D].  Newton uses the exact block Jacobian; the linear system
+ *             splits into one block-bidiagonal system per (batch row, head).  head_size 16, 32 or 64
+ *             (others UNSUPPORTED); no measured budget (max_iters > 0). */
 typedef enum { PARARNN_CELL_LINEAR = 0, PARARNN_CELL_DIAG_GRU = 1, PARARNN_CELL_DIAG_LSTM = 2,
-               PARARNN_CELL_DIAG_SLSTM = 3 } pararnn_cell;
+               PARARNN_CELL_DIAG_SLSTM = 3, PARARNN_CELL_HEAD_GRU = 4 } pararnn_cell;
 
 typedef struct {
   int32_t cell;          /* pararnn_cell */
@@ -88,7 +98,8 @@ typedef struct {
                             D must be even                                                     */
   const void* pre[4];    /* G gate pre-activation planes [B][T][D], caller-precomputed
                             (x_t already projected); 8-byte aligned                            */
-  const float* w;        /* [G][D] diagonal recurrent weights (ignored for LINEAR)             */
+  const float* w;        /* [G][D] diagonal recurrent weights (ignored for LINEAR); HEAD_GRU:
+                            [3][D/head_size][head_size][head_size] dense blocks                   */
   const float* bias;     /* [G][D] biases (ignored for LINEAR)                                 */
   const float* s0;       /* [S][B][D] initial state h_{-1}; NULL = zeros                        */
   const int32_t* cu_seqlens; /* packed sequences, or NULL for one sequence per batch row: n_seqs+1
@@ -99,6 +110,7 @@ typedef struct {
                                 VJP.  Only the offsets strictly between 0 and T matter; the library
                                 does not read them on the host, so it cannot check their order.    */
   int64_t n_seqs;        /* number of packed sequences (ignored when cu_seqlens is NULL)          */
+  int64_t head_size;     /* HEAD_GRU: channels per head (divides D); ignored by the other cells     */
 } pararnn_problem;
 
 /* First Newton iterate when no init_guess is given.  WARM is the GRU / LSTM warm start of the

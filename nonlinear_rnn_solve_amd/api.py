@@ -20,11 +20,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
-CELLS = {"linear": 0, "gru": 1, "lstm": 2, "slstm": 3}
-GATES = {0: 2, 1: 3, 2: 4, 3: 4}
-STATE = {0: 1, 1: 1, 2: 2, 3: 4}
+CELLS = {"linear": 0, "gru": 1, "lstm": 2, "slstm": 3, "head_gru": 4}
+GATES = {0: 2, 1: 3, 2: 4, 3: 4, 4: 3}
+STATE = {0: 1, 1: 1, 2: 2, 3: 4, 4: 1}
+HEAD_GRU = 4
 MAX_ITERS = 64
-ABI_VERSION = 4
+ABI_VERSION = 5
 INIT_ZERO, INIT_WARM = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
           -5: "Newton diverged"}
@@ -48,7 +49,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("cell", ctypes.c_int32), ("pre_dtype", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("pre", ctypes.c_void_p * 4), ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("s0", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int64)]
+                ("s0", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int64),
+                ("head_size", ctypes.c_int64)]
 
 
 class _Opts(ctypes.Structure):
@@ -174,10 +176,18 @@ def _problem(cell, pre, w, bias, s0, cu_seqlens=None):
         if p.shape != pre[0].shape or p.dim() != 3:
             raise ValueError("pre planes must all be [B, T, D]")
     B, T, D = pre[0].shape
+    head_size = 0
     if c != 0:
         _check_dev(w, "w", torch.float32)
         _check_dev(bias, "bias", torch.float32)
-        if tuple(w.shape) != (G, D) or tuple(bias.shape) != (G, D):
+        if c == HEAD_GRU:
+            # w: [3, n_heads, hs, hs] dense blocks (block row = output channel)
+            if w.dim() != 4 or w.shape[0] != G or w.shape[2] != w.shape[3] or w.shape[1] * w.shape[2] != D:
+                raise ValueError("head_gru w must be [3, n_heads, hs, hs] with n_heads * hs = D = %d" % D)
+            head_size = int(w.shape[2])
+            if tuple(bias.shape) != (G, D):
+                raise ValueError("bias must be [G, D] = [%d, %d]" % (G, D))
+        elif tuple(w.shape) != (G, D) or tuple(bias.shape) != (G, D):
             raise ValueError("w and bias must be [G, D] = [%d, %d]" % (G, D))
     _check_dev(s0, "s0", torch.float32)
     if s0 is not None and tuple(s0.shape) != (S, B, D):
@@ -190,6 +200,7 @@ def _problem(cell, pre, w, bias, s0, cu_seqlens=None):
     st.bias = bias.data_ptr() if (c != 0 and bias is not None) else None
     st.s0 = s0.data_ptr() if s0 is not None else None
     st.cu_seqlens, st.n_seqs = _seqlens(cu_seqlens, pre[0].device)
+    st.head_size = head_size
     _same_device(list(pre) + [w if c != 0 else None, bias if c != 0 else None, s0], pre[0].device)
     return st, c, G, S, (B, T, D)
 
@@ -236,7 +247,8 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
                  picard_iters=0):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
-    pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32; s0: [S, B, D].
+    pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32 (head_gru: w is
+    [3, n_heads, hs, hs], the dense recurrent block of each head); s0: [S, B, D].
     max_iters None or 0: the measured budget K*(T) (see newton_budget).
     tol <= 0: exactly max_iters iterations; tol > 0: stop after the first iteration whose max residual
     (evaluated at its input iterate) is below tol.  report=True waits for the stream.

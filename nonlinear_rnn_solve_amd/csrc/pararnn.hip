@@ -45,7 +45,7 @@
 namespace pr {
 
 constexpr int WAVE = 64;
-enum { CELL_LINEAR = 0, CELL_GRU = 1, CELL_LSTM = 2, CELL_SLSTM = 3 };
+enum { CELL_LINEAR = 0, CELL_GRU = 1, CELL_LSTM = 2, CELL_SLSTM = 3, CELL_HEAD_GRU = 4 };
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
 // ------------------------------------------------------------------------------------------------
@@ -1618,6 +1618,8 @@ __global__ __launch_bounds__(256) void k_residual(const void* p0, const void* p1
   if ((threadIdx.x % WAVE) == 0) atomicMax(out, __float_as_uint(m));
 }
 
+#include "head_gru_dev.inc"
+
 }  // namespace pr
 
 // ================================================================================================
@@ -1637,7 +1639,9 @@ uint32_t next_tag() {
 }
 
 int state_size(int cell) { return cell == CELL_SLSTM ? 4 : (cell == CELL_LSTM ? 2 : 1); }
-int gate_count(int cell) { return (cell == CELL_LSTM || cell == CELL_SLSTM) ? 4 : (cell == CELL_GRU ? 3 : 2); }
+int gate_count(int cell) {
+  return (cell == CELL_LSTM || cell == CELL_SLSTM) ? 4 : ((cell == CELL_GRU || cell == CELL_HEAD_GRU) ? 3 : 2);
+}
 
 // workspace: [header 4 KiB: tickets, residual slots][packed-sequence mask][look-back words]
 // [VJP partials]; the mask is (T >> 5) + 2 words (read two at a time by seg_bits)
@@ -1764,11 +1768,15 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 pararnn_status check_problem(const pararnn_problem* pb) {
   if (!pb) return PARARNN_ERR_INVALID_ARG;
-  if (pb->cell < CELL_LINEAR || pb->cell > CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cell < CELL_LINEAR || pb->cell > CELL_HEAD_GRU) return PARARNN_ERR_INVALID_ARG;
   if (pb->pre_dtype != PARARNN_F32 && pb->pre_dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
   if (pb->B < 0 || pb->T < 0 || pb->D < 0) return PARARNN_ERR_INVALID_ARG;
   if (pb->B > (int64_t(1) << 40) || pb->D > (int64_t(1) << 40)) return PARARNN_ERR_INVALID_ARG;
   if (pb->B > 0 && pb->D > 0 && pb->T > INT64_MAX / (pb->B * pb->D) / 4) return PARARNN_ERR_INVALID_ARG;
+  if (pb->cell == CELL_HEAD_GRU) {
+    if (pb->head_size < 1 || (pb->D > 0 && pb->D % pb->head_size != 0)) return PARARNN_ERR_INVALID_ARG;
+    if (pb->head_size != 16 && pb->head_size != 32 && pb->head_size != 64) return PARARNN_ERR_UNSUPPORTED;
+  }
   const int64_t N = pb->B * pb->T * pb->D;
   if (N == 0) return PARARNN_OK;
   if (pb->D % 2 != 0) return PARARNN_ERR_UNSUPPORTED;
@@ -1856,7 +1864,10 @@ NewtonEntry newton_entry_dt(int dt, bool seg) {
   return dt == DT_BF16 ? newton_entry_seg<CELL, DT_BF16>(seg) : newton_entry_seg<CELL, DT_F32>(seg);
 }
 
+NewtonEntry pick_head_newton(const pararnn_problem* pb);
+
 NewtonEntry pick_newton(const pararnn_problem* pb) {
+  if (pb->cell == CELL_HEAD_GRU) return pick_head_newton(pb);
   const bool seg = pb->cu_seqlens != nullptr;
   if (pb->cell == CELL_GRU) return newton_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
   if (pb->cell == CELL_LSTM) return newton_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
@@ -1995,6 +2006,8 @@ VjpEntry pick_vjp(const pararnn_problem* pb) {
   return vjp_entry_dt<CELL_LINEAR>(pb->pre_dtype, seg);
 }
 
+#include "head_gru_host.inc"
+
 }  // namespace
 
 // ================================================================================================
@@ -2069,7 +2082,8 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   if (!op || op->max_iters < 0 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
   if (op->init_mode != PARARNN_INIT_ZERO && op->init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   if (op->picard_iters < 0 || op->picard_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
-  if (op->max_iters == 0 && pb->cell == CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;   // no measured budget
+  if (op->max_iters == 0 && (pb->cell == CELL_SLSTM || pb->cell == CELL_HEAD_GRU))
+    return PARARNN_ERR_INVALID_ARG;   // no measured budget
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
@@ -2153,9 +2167,10 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
 }
 
 int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {
-  if (cell < CELL_LINEAR || cell > CELL_SLSTM || T < 0 || max_iters < 0 || max_iters > PARARNN_MAX_ITERS)
+  if (cell < CELL_LINEAR || cell > CELL_HEAD_GRU || T < 0 || max_iters < 0 || max_iters > PARARNN_MAX_ITERS)
     return PARARNN_ERR_INVALID_ARG;
-  if (max_iters == 0 && cell == CELL_SLSTM) return PARARNN_ERR_INVALID_ARG;   // no measured budget
+  if (max_iters == 0 && (cell == CELL_SLSTM || cell == CELL_HEAD_GRU))
+    return PARARNN_ERR_INVALID_ARG;   // no measured budget
   if (init_mode != PARARNN_INIT_ZERO && init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   return max_iters > 0 ? max_iters : auto_iters(cell, init_mode, T);
 }
@@ -2183,6 +2198,7 @@ pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int d
 
 size_t pararnn_vjp_workspace_bytes(const pararnn_problem* pb) {
   if (check_problem(pb) != PARARNN_OK) return 0;
+  if (pb->cell == CELL_HEAD_GRU) return 0;
   if (problem_N(pb) == 0) return kHeader;
   return pick_vjp(pb).ws(pb);
 }
@@ -2192,6 +2208,7 @@ pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const
                                 void* stream) {
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
+  if (pb->cell == CELL_HEAD_GRU) return PARARNN_ERR_UNSUPPORTED;
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (!s || !g || !d_pre || !aligned(s, 8) || !aligned(g, 8) || !aligned(d_pre, 8)) return PARARNN_ERR_INVALID_ARG;
   if ((lambda_out && !aligned(lambda_out, 8)) || (d_s0 && !aligned(d_s0, 8))) return PARARNN_ERR_INVALID_ARG;

@@ -40,9 +40,10 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
                    ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0),'
                    ' offsetof(pararnn_problem, cu_seqlens), offsetof(pararnn_problem, n_seqs),'
+                   ' offsetof(pararnn_problem, head_size),'
                    ' sizeof(pararnn_newton_opts),'
                    ' offsetof(pararnn_newton_opts, final_residual), offsetof(pararnn_newton_opts, init_mode),'
                    ' offsetof(pararnn_newton_opts, picard_iters),'
@@ -52,7 +53,7 @@ def test_struct_layouts_match_header(tmp_path):
     subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
-            api._Problem.cu_seqlens.offset, api._Problem.n_seqs.offset,
+            api._Problem.cu_seqlens.offset, api._Problem.n_seqs.offset, api._Problem.head_size.offset,
             ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, api._Opts.init_mode.offset,
             api._Opts.picard_iters.offset,
             ctypes.sizeof(api._Report),
@@ -60,9 +61,10 @@ def test_struct_layouts_match_header(tmp_path):
     assert got == want
 
 
-def _problem(cell=1, dtype=0, B=2, T=100, D=64, ptr=4096):
+def _problem(cell=1, dtype=0, B=2, T=100, D=64, ptr=4096, head_size=0):
     p = api._Problem()
     p.cell, p.pre_dtype, p.B, p.T, p.D = cell, dtype, B, T, D
+    p.head_size = head_size
     for i in range(4):
         p.pre[i] = ptr
     p.w = p.bias = ptr
@@ -105,6 +107,11 @@ def test_validation_codes_without_launching(lib):
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 0, -1)) == -1   # negative Picard count
     assert solve(_problem(cell=3), o=api._Opts(0, 0.0, None, 0)) == -1   # sLSTM has no measured budget
+    # head-wise block GRU: the head size must divide D; only 16, 32 and 64 are built; no measured budget
+    assert solve(_problem(cell=4, head_size=0)) == -1
+    assert solve(_problem(cell=4, D=96, head_size=64)) == -1
+    assert solve(_problem(cell=4, D=64, head_size=8)) == -2
+    assert solve(_problem(cell=4, head_size=64), o=api._Opts(0, 0.0, None, 0)) == -1
     p = _problem()
     p.cu_seqlens, p.n_seqs = 4098, 3                          # offsets not 4-byte aligned
     assert solve(p) == -1
@@ -134,7 +141,7 @@ def test_validation_codes_without_launching(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.pararnn_status_string(s).decode() != "unknown status"
-    assert lib.pararnn_abi_version() == api.ABI_VERSION == 4
+    assert lib.pararnn_abi_version() == api.ABI_VERSION == 5
 
 
 def test_binding_refuses_cpu_tensors():
