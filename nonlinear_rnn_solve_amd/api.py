@@ -361,7 +361,8 @@ def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, wan
              cu_seqlens=None):
     """Gradients at trajectory s ([S,B,T,D] float32) for upstream g = dL/dh ([B,T,D] float32).
 
-    Returns dict: d_pre [G,B,T,D]; d_w, d_bias [G,D] (gated cells); d_s0 [S,B,D]; lam [S,B,T,D] if asked.
+    Returns dict: d_pre [G,B,T,D]; d_w, d_bias [G,D] (gated cells; head_gru d_w is [3, n_heads, hs, hs]);
+    d_s0 [S,B,D]; lam [S,B,T,D] if asked.
     """
     lib = load_library()
     st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0, cu_seqlens)
@@ -372,7 +373,8 @@ def scan_vjp(cell, pre, s, g, w=None, bias=None, s0=None, want_lambda=False, wan
     if tuple(s.shape) != (S, B, T, D) or tuple(g.shape) != (B, T, D):
         raise ValueError("s must be [S,B,T,D] and g [B,T,D]")
     d_pre = torch.empty((G, B, T, D), dtype=torch.float32, device=dev)
-    d_w = torch.empty((G, D), dtype=torch.float32, device=dev) if (c != 0 and want_params) else None
+    wshape = tuple(w.shape) if c == HEAD_GRU else (G, D)   # head_gru: [3, n_heads, hs, hs]
+    d_w = torch.empty(wshape, dtype=torch.float32, device=dev) if (c != 0 and want_params) else None
     d_b = torch.empty((G, D), dtype=torch.float32, device=dev) if (c != 0 and want_params) else None
     d_s0 = torch.empty((S, B, D), dtype=torch.float32, device=dev) if want_s0 else None
     lam = torch.empty((S, B, T, D), dtype=torch.float32, device=dev) if want_lambda else None

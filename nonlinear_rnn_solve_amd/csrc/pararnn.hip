@@ -1998,7 +1998,10 @@ VjpEntry vjp_entry_dt(int dt, bool seg) {
   return dt == DT_BF16 ? vjp_entry_seg<CELL, DT_BF16>(seg) : vjp_entry_seg<CELL, DT_F32>(seg);
 }
 
+VjpEntry pick_head_vjp(const pararnn_problem* pb);
+
 VjpEntry pick_vjp(const pararnn_problem* pb) {
+  if (pb->cell == CELL_HEAD_GRU) return pick_head_vjp(pb);
   const bool seg = pb->cu_seqlens != nullptr;
   if (pb->cell == CELL_GRU) return vjp_entry_dt<CELL_GRU>(pb->pre_dtype, seg);
   if (pb->cell == CELL_LSTM) return vjp_entry_dt<CELL_LSTM>(pb->pre_dtype, seg);
@@ -2198,7 +2201,6 @@ pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int d
 
 size_t pararnn_vjp_workspace_bytes(const pararnn_problem* pb) {
   if (check_problem(pb) != PARARNN_OK) return 0;
-  if (pb->cell == CELL_HEAD_GRU) return 0;
   if (problem_N(pb) == 0) return kHeader;
   return pick_vjp(pb).ws(pb);
 }
@@ -2208,7 +2210,6 @@ pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const
                                 void* stream) {
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
-  if (pb->cell == CELL_HEAD_GRU) return PARARNN_ERR_UNSUPPORTED;
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (!s || !g || !d_pre || !aligned(s, 8) || !aligned(g, 8) || !aligned(d_pre, 8)) return PARARNN_ERR_INVALID_ARG;
   if ((lambda_out && !aligned(lambda_out, 8)) || (d_s0 && !aligned(d_s0, 8))) return PARARNN_ERR_INVALID_ARG;

@@ -138,3 +138,94 @@ def test_nan_input_reports_divergence():
     with pytest.raises(api.NewtonDivergenceError) as e:
         solve(inp, max_iters=5, tol=1e-5)
     assert e.value.report.iters == 1 and np.isnan(e.value.report.residuals[0])
+
+
+# ------------------------------------------------------------------------------------------------
+# VJP.  lambda, dL/dU and dL/ds0 relative to max(1, |ref|) <= 1e-4 (as for the diagonal cells: the
+# adjoint recurrence amplifies fp32 rounding).  A parameter entry is a sum over rows n of dU_n x_n,
+# so its error is bounded by the gate gradients' own absolute errors times |x_n| plus the fp32
+# summation: dA and dbias are checked against 1e-5 * sum_n max(1, |dU_n|) |x_n| (1e-5 is the absolute
+# error allowed per gate gradient here; factors such as (c - h) cancel, so a small dU carries an
+# absolute, not a relative, fp32 error).  The bounds come from the oracle's fp64 gate gradients.
+# ------------------------------------------------------------------------------------------------
+def prev_states(traj, s0, cu, T):
+    """[B][T][D] state each step starts from: s0, zero at a sequence start, else s_{t-1}."""
+    prev = np.zeros_like(traj)
+    prev[:, 1:] = traj[:, :-1]
+    prev[:, 0] = 0.0 if s0 is None else s0[0]
+    if cu is not None:
+        for c in cu:
+            if 0 < c < T:
+                prev[:, c] = 0.0
+    return prev
+
+
+def param_bounds(ref, traj, s0, inp, cu):
+    """sum_n max(1, |dU_n|) |x_n| of every dA and dbias entry."""
+    B, T, D, hs = inp.B, inp.T, inp.D, inp.head_size
+    H = D // hs
+    prev = prev_states(traj, s0, cu, T).reshape(B * T, H, hs)
+    dU = np.maximum(1.0, np.abs(ref["d_pre"])).reshape(3, B * T, H, hs)
+    # x of gate c is r_t * s_{t-1}; |r| <= 1, so |s_{t-1}| bounds it
+    x = np.abs(prev)
+    bw = np.einsum("gnhi,nhj->ghij", dU, x)
+    bb = dU.sum(axis=1).reshape(3, D)
+    return bw, bb
+
+
+def vjp_case(inp, s0=None, cu=None, want_lambda=True):
+    prob = oprob(inp, s0, cu)
+    traj = oracle.unroll(prob).astype(np.float32)
+    ref = oracle.vjp(prob, traj.astype(np.float64), inp.g)
+    kw = {"cu_seqlens": torch.from_numpy(cu).cuda()} if cu is not None else {}
+    got = api.scan_vjp("head_gru", dev_pre(inp), dev(traj), dev(inp.g), dev(inp.w), dev(inp.bias), s0=dev(s0),
+                       want_lambda=want_lambda, **kw)
+    got = {k: (v.cpu().numpy() if v is not None else None) for k, v in got.items()}
+    for k in ("d_pre", "lam", "d_s0"):
+        if got.get(k) is not None:
+            err = rel_err(got[k], ref[k])
+            print("  %s max rel err %.3e" % (k, err))
+            assert err <= 1e-4, k
+    bw, bb = param_bounds(ref, traj[0].astype(np.float64), s0, inp, cu)
+    ew = float(np.max(np.abs(got["d_w"] - ref["d_w"]) / np.maximum(bw, 1e-30)))
+    eb = float(np.max(np.abs(got["d_bias"] - ref["d_bias"]) / np.maximum(bb, 1e-30)))
+    print("  d_w err / bound %.3e, d_bias %.3e" % (ew, eb))
+    assert ew <= 1e-5 and eb <= 1e-5
+    return got
+
+
+@pytest.mark.parametrize("hs", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_vjp(hs, dtype, shape):
+    B, T, heads = shape
+    announce("head vjp", hs, dtype, shape)
+    inp = inputs(B, T, heads, hs, dtype, seed=3600 + T + hs, with_grad=True)
+    s0 = synth.random_state(1, B, heads * hs, seed=34)
+    vjp_case(inp, s0)
+
+
+def test_vjp_packed_sequences_and_zero_state():
+    announce("head vjp packed")
+    B, T, heads, hs = 2, 90, 2, 32
+    inp = inputs(B, T, heads, hs, seed=3700, with_grad=True)
+    cu = synth.packed_offsets(T, seed=6, mean_len=18, forced=(16, 17, 33, 89))
+    vjp_case(inp, None, cu)
+
+
+def test_vjp_example_shape_and_reproducible():
+    announce("head vjp example shape")
+    B, T, heads, hs = 4, 64, 8, 64
+    inp = inputs(B, T, heads, hs, seed=3800, with_grad=True)
+    got = vjp_case(inp, want_lambda=False)
+    again = api.scan_vjp("head_gru", dev_pre(inp), dev(oracle.unroll(oprob(inp)).astype(np.float32)), dev(inp.g),
+                         dev(inp.w), dev(inp.bias))
+    for k in ("d_pre", "d_w", "d_bias", "d_s0"):
+        assert np.array_equal(again[k].cpu().numpy(), got[k]), k    # fixed-order sums: bitwise equal
+
+
+def test_vjp_long_sequence():
+    announce("head vjp long")
+    B, T, heads, hs = 2, 1500, 4, 64
+    inp = inputs(B, T, heads, hs, "bf16", seed=3900, with_grad=True)
+    vjp_case(inp, synth.random_state(1, B, heads * hs, seed=35), want_lambda=False)
