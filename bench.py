@@ -10,7 +10,8 @@ dL/dh ~ N(0, 1).  Other workloads (--workload 0..3) time one Newton solve or one
 
 --variants times the same workload with the options built on the method (warm start, the measured
 budget K*(T), packed sequences) and prints one JSON line per variant instead; --kstar times the
-automatic budget over a grid of sequence lengths.  Neither is the benchmark line.
+automatic budget over a grid of sequence lengths; --slstm and --head time the diagonal sLSTM and the
+head-wise block GRU.  None of them is the benchmark line.
 
 Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
 iterations the solve ran (a linear scan counts K = 1).  roofline: the steady-state fused Newton
@@ -98,6 +99,7 @@ def main():
     ap.add_argument("--variants", action="store_true", help="time warm start / K* budget / packed variants")
     ap.add_argument("--kstar", action="store_true", help="time the automatic budget over a grid of lengths")
     ap.add_argument("--slstm", action="store_true", help="time the diagonal sLSTM solve and VJP over a grid of lengths")
+    ap.add_argument("--head", action="store_true", help="time the head-wise block GRU solve and VJP")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device-to-device copy of this many MiB "
                          "(same-box bandwidth context, and the known-size kernel that calibrates HBM counters)")
@@ -121,6 +123,8 @@ def main():
     if args.kstar:
         kstar_bench(torch, dev, args)
         return
+    if args.head:
+        return head_bench(torch, dev, args)
     if args.slstm:
         slstm_bench(torch, dev, args)
         return
@@ -353,6 +357,39 @@ def slstm_bench(torch, dev, args):
                           "iters": iters, "converged": rep_.converged, "final_residual": rep_.final_residual,
                           "ms_per_solve_and_vjp": ms, "iteration_kernel_ms": kern,
                           "iteration_gbs": per_elem * N / (kern * 1e-3) / 1e9, "vjp_ms": e0.elapsed_time(e1),
+                          "channel_tokens_per_s": N * iters / (ms * 1e-3)}), flush=True)
+        del pre, out, g
+        torch.cuda.empty_cache()
+
+
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def head_bench(torch, dev, args):
+    """The head-wise block GRU (head size 64, fp32) on three shapes: the pararnn-torch README's example
+    (ParaGRU(512, 512, mix="head", n_heads=8) on a (4, 64, 512) batch), a larger batch of such short
+    sequences, and longer sequences.  Newton from the zero guess until the max residual is below 1e-5
+    (at most 8 iterations), then the VJP.  The iteration is MFMA-bound: per step and head it forms the
+    dense Jacobian block (A_c diag(s) A_r, 2 hs^3 flops) and multiplies it into the chunk's product
+    (2 hs^3), so iteration_tflops = 4 hs^3 B T H / iteration time against the fp32 MFMA peak (the
+    gate, carry and finishing matrix-vector work is counted in the time, not in the flops)."""
+    from nonlinear_rnn_solve_amd import api, synth
+    hs, D = 64, 512
+    for B, T in ((4, 64), (16, 64), (16, 1024)):
+        inp = synth.make_inputs("head_gru", B, T, D, seed=5000 + B + T, with_grad=True, head_size=hs)
+        pre, w, b, g = device_inputs(torch, dev, inp)
+        out = torch.empty((1, B, T, D), dtype=torch.float32, device=dev)
+        ms, iters, kern = time_solve(torch, api, "head_gru", pre, w, b, g, out, args.steps, args.warmup, vjp=True,
+                                     max_iters=8, tol=1e-5)
+        ms_solve, _, _ = time_solve(torch, api, "head_gru", pre, w, b, g, out, args.steps, args.warmup,
+                                    max_iters=8, tol=1e-5)
+        flops = 4.0 * hs ** 3 * B * T * (D // hs)
+        N = B * T * D
+        print(json.dumps({"cell": "head_gru", "storage": "f32", "B": B, "T": T, "D": D, "head_size": hs,
+                          "tol": 1e-5, "iters": iters, "ms_per_solve": ms_solve, "ms_per_solve_and_vjp": ms,
+                          "iteration_ms": kern, "iteration_tflops": flops / (kern * 1e-3) / 1e12,
+                          "mfma_fp32_peak_tflops": MFMA_FP32_PEAK_TFLOPS,
+                          "frac": flops / (kern * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
                           "channel_tokens_per_s": N * iters / (ms * 1e-3)}), flush=True)
         del pre, out, g
         torch.cuda.empty_cache()
