@@ -12,10 +12,12 @@ from nonlinear_rnn_solve_amd import api, synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cell,dtype,shape,tol", [("gru", "bf16", (1, 5000, 64), 1e-5), ("lstm", "f32", (2, 700, 34), 0.0)])
+@pytest.mark.parametrize("cell,dtype,shape,tol", [("gru", "bf16", (1, 5000, 64), 1e-5), ("lstm", "f32", (2, 700, 34), 0.0),
+                                                  ("head_gru", "f32", (2, 300, 128), 1e-5)])
 def test_captured_solve_and_vjp_replay_like_eager(cell, dtype, shape, tol):
     B, T, D = shape
-    inp = synth.make_inputs(cell, B, T, D, dtype=dtype, seed=3100 + T, with_grad=True)
+    inp = synth.make_inputs(cell, B, T, D, dtype=dtype, seed=3100 + T, with_grad=True,
+                            head_size=64 if cell == "head_gru" else None)
     pre, w, b, g = dev_pre(inp), dev(inp.w), dev(inp.bias), dev(inp.g)
     lin = synth.make_inputs("linear", B, T, D, seed=3101)
     a_, b_ = dev(lin.pre[0]), dev(lin.pre[1])
