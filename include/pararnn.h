@@ -146,10 +146,13 @@ typedef struct {          /* (host) */
 
 /* ------------------------------------------------------------------------------------------------
  * pararnn_newton_solve -- Newton solve of F(H) = 0 for the given cell (pararnn-torch README,
- * "Method"; ParaRNN abstract).  Each iteration is ONE fused kernel: it evaluates the residual and
- * the per-channel Jacobian (scalar for GRU, 2x2 for LSTM) at the current iterate, forms the affine
- * scan elements of the linearised recurrence in registers, combines them across the workgroup and
- * across time chunks (decoupled look-back), and writes H^{k+1} = H^k + delta in place into s_out.
+ * "Method"; ParaRNN abstract).  For the diagonal cells each iteration is ONE fused kernel: it
+ * evaluates the residual and the per-channel Jacobian (scalar for GRU, 2x2 for LSTM, 4x4 for sLSTM)
+ * at the current iterate, forms the affine scan elements of the linearised recurrence in registers,
+ * combines them across the workgroup and across time chunks (decoupled look-back), and writes
+ * H^{k+1} = H^k + delta in place into s_out.  For HEAD_GRU an iteration is three kernels: each
+ * chunk's composed map of dense Jacobian blocks (MFMA), a carry of the state across chunks, and a
+ * per-step replay that writes H^{k+1} in place.
  *   s_out  [S][B][T][D] fp32 output trajectory (H^{iters}).  Must not overlap pre/w/bias/s0.
  *   report (host, nullable): when given, the call waits for the stream and fills it.
  * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE before any launch; HIP after a failed launch;
@@ -165,8 +168,8 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_n
  * [final residual]; report.  All share one workspace and stream; `opts` must be the same object
  * contents in every call of one solve.
  *   prepare  -- clears the workspace's counters and look-back words (one small kernel).
- *   iterate  -- launches iteration k (0 <= k < max_iters): one fused kernel reading H^k (init_guess
- *               for k = 0, else s_out) and writing H^{k+1} into s_out.  In tolerance mode a kernel
+ *   iterate  -- launches iteration k (0 <= k < max_iters): the kernels of one iteration, reading H^k
+ *               (init_guess for k = 0, else s_out) and writing H^{k+1} into s_out.  In tolerance mode a kernel
  *               whose earlier residual met the stop rule exits at once without touching s_out.
  *   report   -- (host) optionally launches the final-residual pass, waits for the stream and fills
  *               `report`; returns DIVERGED as pararnn_newton_solve does.                              */
