@@ -105,8 +105,8 @@ def main():
                          "(same-box bandwidth context, and the known-size kernel that calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported (the hot path shards "
-              "without communication, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus %d is not supported (independent channels shard "
+              "across GPUs without communication; no multi-GPU path is built)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -367,7 +367,7 @@ MFMA_FP32_PEAK_TFLOPS = 157.3
 
 def head_bench(torch, dev, args):
     """The head-wise block GRU (head size 64, fp32) on three shapes: the pararnn-torch README's example
-    (ParaGRU(512, 512, mix="head", n_heads=8) on a (4, 64, 512) batch), a larger batch of such short
+    (a head GRU of width 512 with 8 heads, on 4 sequences of 64 steps), a larger batch of such short
     sequences, and longer sequences.  Newton from the zero guess until the max residual is below 1e-5
     (at most 8 iterations), then the VJP.  The iteration is MFMA-bound: per step and head it forms the
     dense Jacobian block (A_c diag(s) A_r, 2 hs^3 flops) and multiplies it into the chunk's product

@@ -79,7 +79,7 @@ typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
  *             (at a tie of the max the forget branch is taken).  Its Newton iteration wants a few
  *             Picard sweeps first (opts.picard_iters); it has no measured budget (max_iters > 0).
  *  HEAD_GRU  G=3 (z, r, c), S=1: the head-wise block GRU of the pararnn-torch README ("Usage":
- *             ParaGRU with mix="head" and n_heads, block-diagonal A_*, factorized Newton).  The D
+ *             ParaGRU in its head-wise mixing mode: block-diagonal recurrent matrices, factorized Newton).  The D
  *             channels form D / head_size heads of head_size consecutive channels; each gate's
  *             recurrent matrix is block-diagonal with one dense head_size x head_size block per head:
  *              z = sig(U_z + A_z h + b_z),  r = sig(U_r + A_r h + b_r),

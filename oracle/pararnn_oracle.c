@@ -757,7 +757,7 @@ int or_vjp(const or_problem* p, const double* s, const float* g, double* d_pre, 
 /* ------------------------------------------------------------------------ */
 /*
  * pararnn-torch README, "Usage" (Dreamer-style block GRU: ParaGRU with
- * mix="head" and n_heads; block-diagonal A_*, factorized Newton) and "News"
+ * the head-wise mixing mode and a head count; block-diagonal recurrent matrices, factorized Newton) and "News"
  * (factorized Newton for that cell).  The page prints no equations.  Reading:
  * the channels split into n_heads heads of hs = D / n_heads consecutive
  * channels; each gate's recurrent matrix A_g is block-diagonal with one dense

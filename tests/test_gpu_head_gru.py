@@ -105,7 +105,7 @@ def test_tolerance_mode_report_and_final_residual():
 
 
 def test_example_shape_of_the_pages():
-    # ParaGRU(512, 512, mix="head", n_heads=8) applied to a (4, 64, 512) batch (pararnn-torch README, "Usage")
+    # the pararnn-torch README's example ("Usage"): a head GRU of width 512 with 8 heads on 4 sequences of 64 steps
     B, T, heads, hs = 4, 64, 8, 64
     announce("head newton example shape")
     inp = inputs(B, T, heads, hs, seed=3300)

@@ -1,5 +1,5 @@
 """Pins for the oracle's head-wise block GRU (pararnn-torch README, "Usage": the Dreamer-style
-ParaGRU with mix="head" and n_heads, whose recurrent matrices are block-diagonal; "News": its
+ParaGRU in its head-wise mixing mode, whose recurrent matrices are block-diagonal; "News": its
 factorized Newton).
 
 The oracle's cell applies the reset gate before the candidate's matrix, c = tanh(U_c + A_c (r*h) + b_c),
