@@ -357,7 +357,8 @@ def slstm_bench(torch, dev, args):
                           "iters": iters, "converged": rep_.converged, "final_residual": rep_.final_residual,
                           "ms_per_solve_and_vjp": ms, "iteration_kernel_ms": kern,
                           "iteration_gbs": per_elem * N / (kern * 1e-3) / 1e9, "vjp_ms": e0.elapsed_time(e1),
-                          "channel_tokens_per_s": N * iters / (ms * 1e-3)}), flush=True)
+                          "channel_tokens_per_s": N * iters / (ms * 1e-3),
+                          "cpu_oracle": slstm_oracle_rate(inp, 8)}), flush=True)
         del pre, out, g
         torch.cuda.empty_cache()
 
@@ -385,14 +386,46 @@ def head_bench(torch, dev, args):
                                     max_iters=8, tol=1e-5)
         flops = 4.0 * hs ** 3 * B * T * (D // hs)
         N = B * T * D
+        cpu = head_oracle_rate(inp, iters)
         print(json.dumps({"cell": "head_gru", "storage": "f32", "B": B, "T": T, "D": D, "head_size": hs,
                           "tol": 1e-5, "iters": iters, "ms_per_solve": ms_solve, "ms_per_solve_and_vjp": ms,
                           "iteration_ms": kern, "iteration_tflops": flops / (kern * 1e-3) / 1e12,
                           "mfma_fp32_peak_tflops": MFMA_FP32_PEAK_TFLOPS,
                           "frac": flops / (kern * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
-                          "channel_tokens_per_s": N * iters / (ms * 1e-3)}), flush=True)
+                          "channel_tokens_per_s": N * iters / (ms * 1e-3), "cpu_oracle": cpu}), flush=True)
         del pre, out, g
         torch.cuda.empty_cache()
+
+
+def head_oracle_rate(inp, iters):
+    """The fp64 oracle's Newton solve + VJP on one batch row (every head, full T) of a head-GRU
+    workload, as channel-tokens/s (B*T*D*K per second scaled to the sample), for context."""
+    import oracle
+    threads = cpu_threads()
+    pre = [np.ascontiguousarray(p[:1]) for p in inp.pre]
+    prob = oracle.Problem("head_gru", pre, inp.w, inp.bias, head_size=inp.head_size)
+    t0 = time.perf_counter()
+    H, res, k, conv, rc = oracle.newton(prob, 8, tol=1e-5, nthreads=threads)
+    oracle.vjp(prob, H, np.ascontiguousarray(inp.g[:1]), want_lambda=False, nthreads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": inp.T * inp.D * k / sec, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "1 of %d batch rows, full T=%d, Newton (%d iterations) + VJP; %.2f s" % (inp.B, inp.T, k, sec)}
+
+
+def slstm_oracle_rate(inp, picard, n_channels=64):
+    """The fp64 oracle's sLSTM solve (Picard sweeps, then Newton to 1e-5) + VJP on a sample of channels at
+    full T, as channel-tokens/s, for context."""
+    import oracle
+    threads = cpu_threads()
+    ds = np.arange(min(n_channels, inp.D))
+    pre = [np.ascontiguousarray(p[:1, :, ds]) for p in inp.pre]
+    prob = oracle.Problem("slstm", pre, inp.w[:, ds], inp.bias[:, ds])
+    t0 = time.perf_counter()
+    H, res, k, conv, rc = oracle.newton(prob, 40, tol=1e-5, picard=picard, nthreads=threads)
+    oracle.vjp(prob, H, np.ascontiguousarray(inp.g[:1, :, ds]), want_lambda=False, nthreads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": len(ds) * inp.T * k / sec, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d channels of batch row 0, full T=%d, %d updates + VJP; %.2f s" % (len(ds), inp.T, k, sec)}
 
 
 def copy_gbs(torch, dev, mib=1024, reps=5):
