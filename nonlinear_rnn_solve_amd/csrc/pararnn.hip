@@ -242,6 +242,51 @@ DEV void apply(const Aff<S>& m, float (&x)[S]) {
   for (int i = 0; i < S; ++i) x[i] = y[i];
 }
 
+// compose and apply for an element whose matrix is known to be zero outside MASK (bit i*S + k set where
+// A[i][k] may be nonzero): the skipped terms are exact zeros, so the result equals compose / apply for finite
+// values, with fewer multiply-adds (the sLSTM's 4x4 Jacobian has four structural zeros and a sparse row)
+template <int S, uint32_t MASK>
+DEV Aff<S> compose_masked(const Aff<S>& lat, const Aff<S>& ear) {
+  Aff<S> r;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+        if ((MASK >> (i * S + k)) & 1u) acc = fmaf(lat.A[i * S + k], ear.A[k * S + j], acc);
+      r.A[i * S + j] = acc;
+    }
+    float acc = lat.b[i];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      if ((MASK >> (i * S + k)) & 1u) acc = fmaf(lat.A[i * S + k], ear.b[k], acc);
+    r.b[i] = acc;
+  }
+  return r;
+}
+template <int S, uint32_t MASK>
+DEV void apply_masked(const Aff<S>& m, float (&x)[S]) {
+  float y[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    float acc = m.b[i];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      if ((MASK >> (i * S + k)) & 1u) acc = fmaf(m.A[i * S + k], x[k], acc);
+    y[i] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < S; ++i) x[i] = y[i];
+}
+template <int S>
+constexpr uint32_t kFullMask = (S * S >= 32) ? 0xFFFFFFFFu : ((1u << (S * S)) - 1u);
+// the sLSTM Jacobian (state c, n, m, h): c' and n' do not depend on n and c respectively, m' not on c or n
+constexpr uint32_t kSlstmJMask = 0xFCEDu;
+// its transpose (the VJP's elements)
+constexpr uint32_t kSlstmJtMask = 0xFFA9u;
+
 template <int S>
 DEV float aff_get(const Aff<S>& m, int k) { return k < S * S ? m.A[k] : m.b[k - S * S]; }
 template <int S>
@@ -536,9 +581,9 @@ void k_tile(const typename Op::Args a) {
   Aff<S> excl[V];                                      // slices of this wave before mine, composed
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    Aff<S> g = aff_id<S>();
+    Aff<S> g = ln.e[v][REV ? L - 1 : 0];   // the first element itself: no composition with the identity
 #pragma unroll
-    for (int s = 0; s < L; ++s) g = compose(ln.e[v][REV ? L - 1 - s : s], g);
+    for (int s = 1; s < L; ++s) g = Op::compose_elem(ln.e[v][REV ? L - 1 - s : s], g);
     excl[v] = aff_id<S>();
     if constexpr (TS > 1) {
       // inclusive scan over slices (Hillis-Steele on lanes LPR apart), then shift by one slice
@@ -866,6 +911,8 @@ struct LinearOp {
     Aff<S> e[V][L];
   };
   static DEV bool skip(const Args&) { return false; }
+  static constexpr uint32_t EMASK = kFullMask<S>;
+  static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
     load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
   }
@@ -915,7 +962,7 @@ struct LinearOp {
       const int i = REV ? L - 1 - s : s;
       if (i >= tl.nvalid) continue;
 #pragma unroll
-      for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
+      for (int v = 0; v < V; ++v) apply_masked<S, EMASK>(ln.e[v][i], x[v]);
 #pragma unroll
       for (int k = 0; k < S; ++k) {
         float o[V];
@@ -969,6 +1016,8 @@ struct NewtonOp {
     }
     return false;
   }
+  static constexpr uint32_t EMASK = CELL == CELL_SLSTM ? kSlstmJMask : kFullMask<S>;   // elements are J_t
+  static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
     load_s0<S, V>(a.s0, a.B, a.c.D, tl, x);
   }
@@ -1207,7 +1256,7 @@ struct NewtonOp {
     for (int i = 0; i < L; ++i) {
       if (i >= tl.nvalid) continue;
 #pragma unroll
-      for (int v = 0; v < V; ++v) apply(ln.e[v][i], x[v]);
+      for (int v = 0; v < V; ++v) apply_masked<S, EMASK>(ln.e[v][i], x[v]);
 #pragma unroll
       for (int k = 0; k < S; ++k) {
         float o[V];
@@ -1261,6 +1310,8 @@ struct VjpOp {
     float ac[V];          // GRU: a_c, for d h'/d u_r
   };
   static DEV bool skip(const Args&) { return false; }
+  static constexpr uint32_t EMASK = CELL == CELL_SLSTM ? kSlstmJtMask : kFullMask<S>;   // elements are J_{t+1}^T
+  static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
@@ -1401,7 +1452,7 @@ struct VjpOp {
         float du[G][V], lam[S][V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          apply(ln.e[v][i], x[v]);
+          apply_masked<S, EMASK>(ln.e[v][i], x[v]);
           const VjpStash<CELL>& st = ln.st[v][i];
 #pragma unroll
           for (int k = 0; k < S; ++k) lam[k][v] = x[v][k];
