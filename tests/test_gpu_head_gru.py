@@ -229,3 +229,14 @@ def test_vjp_long_sequence():
     B, T, heads, hs = 2, 1500, 4, 64
     inp = inputs(B, T, heads, hs, "bf16", seed=3900, with_grad=True)
     vjp_case(inp, synth.random_state(1, B, heads * hs, seed=35), want_lambda=False)
+
+
+def test_empty_problems_are_no_ops():
+    announce("head empty")
+    for B, T in ((0, 10), (2, 0)):
+        inp = inputs(max(B, 1), max(T, 1), 2, 16, seed=4000)
+        pre = [torch.empty((B, T, 32), device="cuda") for _ in range(3)]
+        h, rep = api.newton_solve("head_gru", pre, dev(inp.w), dev(inp.bias), max_iters=3, tol=1e-5)
+        assert h.shape == (1, B, T, 32) and rep.iters == 0 and rep.converged
+        gr = api.scan_vjp("head_gru", pre, h, torch.empty((B, T, 32), device="cuda"), dev(inp.w), dev(inp.bias))
+        assert gr["d_pre"].shape == (3, B, T, 32)

@@ -66,3 +66,51 @@ def test_newton_and_vjp_beyond_32_bit_offsets():
     e_dw = float(np.max(np.abs(dw - vref["d_w"]) / (1 + np.abs(vref["d_w"]))))
     print("  vjp lambda", e_lam, "d_pre", e_dp, "d_w", e_dw, flush=True)
     assert e_lam <= 1e-4 and e_dp <= 1e-4 and e_dw <= 1e-4
+
+
+def test_head_gru_beyond_32_bit_element_offsets():
+    """The head-wise block GRU with more than 2^31 elements per plane (B=4200, T=1000, D=512: 2.15e9), so
+    that element offsets of the later batch rows exceed 32 bits; fp32 gate inputs tiled from a seeded pool of
+    2^26 + 7 draws (the period is prime to every stride, so rows differ).  The Newton iterate and the VJP are
+    checked on sampled batch rows (all heads) against the oracle; the last row's offsets exceed 2^31."""
+    Bh, Th, Dh, hs = 4200, 1000, 512, 64
+    print("[case] head max size", Bh, Th, Dh, flush=True)
+    rng = np.random.Generator(np.random.PCG64(2950))
+    N = Bh * Th * Dh
+    assert N > (1 << 31)
+    pool = rng.standard_normal(size=(1 << 26) + 7, dtype=np.float32)
+    planes = [np.resize(np.roll(pool, 977 * g), N).reshape(Bh, Th, Dh) for g in range(3)]
+    w = ((rng.random(size=(3, Dh // hs, hs, hs), dtype=np.float32) - np.float32(0.5)) *
+         np.float32(2.0 / np.sqrt(hs))).astype(np.float32)
+    bias = (rng.standard_normal(size=(3, Dh), dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    pre = [torch.from_numpy(p).cuda() for p in planes]
+    wt, bt = torch.from_numpy(w).cuda(), torch.from_numpy(bias).cuda()
+    K = 2
+    H, rep = api.newton_solve("head_gru", pre, wt, bt, max_iters=K)
+    rows = [0, 2049, Bh - 1]
+    sub = [np.ascontiguousarray(p[rows]) for p in planes]
+    prob = oracle.Problem("head_gru", sub, w, bias, head_size=hs)
+    ref, res, *_ = oracle.newton(prob, K)
+    got = H[0][torch.tensor(rows, device="cuda")].cpu().numpy()
+    err = max_abs(got, ref[0])
+    print("  newton max abs err", err, "residuals", rep.residuals, "oracle", list(res), flush=True)
+    assert err <= 1e-5
+    assert all(r >= q * (1 - 1e-3) for r, q in zip(rep.residuals, res))
+    api._ws_cache.clear()           # release the Newton workspace (86 GB) before the VJP's
+    torch.cuda.empty_cache()
+    g = torch.zeros((Bh, Th, Dh), device="cuda")
+    gs = np.random.default_rng(2951).standard_normal((len(rows), Th, Dh)).astype(np.float32)
+    g[torch.tensor(rows, device="cuda")] = torch.from_numpy(gs).cuda()
+    out = api.scan_vjp("head_gru", pre, H, g, wt, bt, want_s0=False)
+    traj = got.astype(np.float64)[None]
+    vref = oracle.vjp(prob, traj, gs)
+    dpre = out["d_pre"][:, torch.tensor(rows, device="cuda")].cpu().numpy()
+    e_dp = float(np.max(np.abs(dpre - vref["d_pre"]) / np.maximum(1, np.abs(vref["d_pre"]))))
+    # only the sampled rows carry a gradient, so the parameter sums are the oracle's over those rows
+    dw = out["d_w"].cpu().numpy()
+    e_dw = float(np.max(np.abs(dw - vref["d_w"]) / (1 + np.abs(vref["d_w"]))))
+    print("  vjp d_pre", e_dp, "d_w", e_dw, flush=True)
+    assert e_dp <= 1e-4 and e_dw <= 1e-4
+    del pre, H, g, out
+    api._ws_cache.clear()
+    torch.cuda.empty_cache()
