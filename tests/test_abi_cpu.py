@@ -83,6 +83,16 @@ def test_workspace_queries(lib):
     assert lib.pararnn_vjp_workspace_bytes(ctypes.byref(_problem(cell=2))) > 0
     p.D = 0
     assert lib.pararnn_newton_workspace_bytes(ctypes.byref(p), None) == 4096   # empty problem: header only
+    # head-wise block GRU: chunk aggregates (hs^2 + hs floats per chunk), entering states and 6 factors per
+    # element; the VJP adds the parameter partials
+    h = _problem(cell=4, B=4, T=64, D=512, head_size=64)
+    nh = lib.pararnn_newton_workspace_bytes(ctypes.byref(h), None)
+    assert nh > 6 * 4 * 4 * 64 * 512                                # at least the per-step factors
+    assert lib.pararnn_vjp_workspace_bytes(ctypes.byref(h)) > nh
+    h.T = 1024
+    assert lib.pararnn_newton_workspace_bytes(ctypes.byref(h), None) > 10 * nh
+    h.head_size = 8                                                  # not built
+    assert lib.pararnn_newton_workspace_bytes(ctypes.byref(h), None) == 0
 
 
 def test_validation_codes_without_launching(lib):
