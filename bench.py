@@ -14,12 +14,18 @@ automatic budget over a grid of sequence lengths; --slstm and --head time the di
 head-wise block GRU.  None of them is the benchmark line.
 
 Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
-iterations the solve ran (a linear scan counts K = 1).  roofline: the steady-state fused Newton
-iteration kernel (or the scan kernel), algorithmic bytes per element x elements / its mean
-launch duration from HIP events on the launch stream; roofline.copy_gbs is a device-to-device copy's
-bandwidth on the same GPU, for context.  cpu_baseline: the fp64 CPU oracle on a bounded sample of
-channels of the same workload (value: its Newton solve + VJP; unroll_value: its sequential unroll,
-the exact solution).
+iterations the solve ran (a linear scan counts K = 1).  The solve runs its iterations fused: one
+launch that reads the gate inputs once and keeps the trajectory in registers (fuse_iters = the
+iteration count of the untimed solve before the timed region, as a loop of solves would speculate;
+the result is the same bit for bit for any value).  roofline: that launch is bound by vector ALU
+issue, so it is rated in algorithmic flops (flops per element-iteration of the cell, its scan element,
+composition and update, as the kernel's arithmetic is written: fma = 2, add / mul / exp2 / rcp = 1) x
+elements x iterations / the solve's duration from HIP events on the launch stream (the fused launch
+plus the solve's empty launches), against the fp32 vector peak; for the linear scan, HBM bytes as
+before.  roofline.copy_gbs is a device-to-device copy's bandwidth on the same GPU, for context;
+per_iteration_kernel is the one-launch-per-iteration kernel's HBM figure, timed after the timed
+region.  cpu_baseline: the fp64 CPU oracle on a bounded sample of channels of the same workload
+(value: its Newton solve + VJP; unroll_value: its sequential unroll, the exact solution).
 """
 from __future__ import annotations
 
@@ -36,6 +42,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "channel-tokens/s per Newton solve (B*T*D*K/s) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X vector fp32 (256 CUs, 2.4 GHz; the packed-fp32 figure)
+
+# algorithmic flops of one element-iteration of a Newton solve (fma = 2, add / mul / exp2 / rcp = 1):
+#   GRU: cell value and Jacobian 44, scan element (residual, b = f - J h) 3, composition 3, update 2
+#   LSTM: cell 64, elements 10, 2x2 composition 20, update 8
+FLOPS_PER_ELEM_ITER = {"gru": 52, "lstm": 102}
+
+
+def fused_bytes(cell: str, dtype: str) -> int:
+    """HBM bytes per element of a fused solve from the zero start: the gate inputs once, H written once."""
+    esz = 2 if dtype == "bf16" else 4
+    G, S = (3, 1) if cell == "gru" else (4, 2)
+    return G * esz + S * 4
 
 # algorithmic HBM bytes per element of one launch of the dominant kernel
 #   GRU steady iteration: read U (3 planes) + read H^k + write H^{k+1}
@@ -146,16 +165,7 @@ def main():
         out = out[0]
 
     stream = torch.cuda.current_stream(dev)
-    iter_events = []     # per step: list of (k, start, end)
-
-    def hook(k, phase, rec):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record(stream)
-        if phase == "before":
-            rec.append([k, ev, None])
-        else:
-            rec[-1][2] = ev
-
+    iter_events = []     # per step: list of (k, start, end) around the solve's (or the scan's) launches
     vjp_events = []
 
     # Timed steps are enqueued back to back with no host synchronisation (as a training loop would run
@@ -173,8 +183,13 @@ def main():
             rec.append([0, e0, e1])
             iters = 1
         else:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             _, rep = api.newton_solve(wl.cell, pre, w, b, max_iters=wl.max_iters, tol=wl.tol, out=out,
-                                      on_iteration=lambda k, ph: hook(k, ph, rec), report=report)
+                                      report=report, fuse_iters=fuse[0])
+            e1.record(stream)
+            rec.append([0, e0, e1])   # the solve's launches
             iters = rep.iters if rep is not None else None
             if wl.vjp:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -188,9 +203,15 @@ def main():
             iter_events.append(rec)
         return iters
 
+    fuse = [0]   # the library's choice until a solve has reported its iteration count
     for _ in range(args.warmup):
         step(False)
     iters = step(False, report=True)
+    if wl.cell != "linear":
+        fuse[0] = min(iters, api.MAX_FUSE)
+        step(False)
+        if step(False, report=True) != iters:
+            raise RuntimeError("the iteration count changed with the fused launch length")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -201,31 +222,44 @@ def main():
     if step(False, report=True) != iters:
         raise RuntimeError("the iteration count changed between steps")
 
-    # dominant kernel: the steady-state fused Newton iteration (k >= 1 and doing work), or the scan
-    durs = []
-    for rec in iter_events:
-        for k, e0, e1 in rec:
-            if wl.cell == "linear" or (1 <= k < iters):
-                durs.append(e0.elapsed_time(e1))
-    if not durs:  # a solve of one iteration: only the zero-guess launch exists
-        durs = [e0.elapsed_time(e1) for rec in iter_events for k, e0, e1 in rec if k < iters]
-    kern_ms = float(np.mean(durs))
-    per_elem = algo_bytes(wl.cell, wl.dtype)
-    achieved = per_elem * N / (kern_ms * 1e-3) / 1e9
+    # dominant kernel: the fused Newton launch (the solve's launches, timed together), or the scan
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for rec in iter_events for k, e0, e1 in rec]))
     value = N * iters / (ms_per_step * 1e-3)
-    kernel_name = "k_tile<LinearOp>" if wl.cell == "linear" else "k_tile<NewtonOp> (iterations k>=1)"
     traffic = measured_traffic(wl.name)
+    config = {"workload": wl.name, "cell": wl.cell, "B": wl.B, "T": wl.T, "D": wl.D, "storage": wl.dtype,
+              "tol": wl.tol, "max_iters": wl.max_iters, "iters": iters, "vjp": wl.vjp}
+    if wl.cell == "linear":
+        per_elem = algo_bytes(wl.cell, wl.dtype)
+        achieved = per_elem * N / (kern_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "k_tile<LinearOp>",
+                    "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
+                    "copy_gbs": copy_gbs(torch, dev)}
+    else:
+        config["fuse_iters"] = fuse[0]
+        flops = FLOPS_PER_ELEM_ITER[wl.cell] * N * iters
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        fb = fused_bytes(wl.cell, wl.dtype)
+        roofline = {"bound": "alu", "achieved": achieved, "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / VALU_FP32_PEAK_TFLOPS, "traffic": traffic,
+                    "kernel": "k_fused<NewtonOp>: the solve's %d iterations in %d launch(es)"
+                              % (iters, -(-iters // fuse[0])),
+                    "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops,
+                    "kernel_ms": kern_ms, "bytes_per_elem": fb, "hbm_gbs": fb * N / (kern_ms * 1e-3) / 1e9,
+                    "copy_gbs": copy_gbs(torch, dev)}
     line = {
         "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "cell": wl.cell, "B": wl.B, "T": wl.T, "D": wl.D, "storage": wl.dtype,
-                   "tol": wl.tol, "max_iters": wl.max_iters, "iters": iters, "vjp": wl.vjp},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel_name,
-                     "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
-                     "copy_gbs": copy_gbs(torch, dev)},
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": config, "roofline": roofline,
     }
+    if wl.cell != "linear":
+        # the one-launch-per-iteration kernel (steady iterations k >= 1), timed after the timed region
+        _, _, it_ms = time_solve(torch, api, wl.cell, pre, w, b, g, out, 1, 1, max_iters=wl.max_iters,
+                                 tol=wl.tol, fuse_iters=1)
+        per_elem = algo_bytes(wl.cell, wl.dtype)
+        gbs = per_elem * N / (it_ms * 1e-3) / 1e9
+        line["per_iteration_kernel"] = {"kernel": "k_tile<NewtonOp> (iterations k>=1, fuse_iters=1)", "ms": it_ms,
+                                        "bytes_per_elem": per_elem, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     if vjp_events:
         vms = float(np.mean([a.elapsed_time(b2) for a, b2 in vjp_events]))
         line["vjp"] = {"ms": vms, "bytes_per_elem": vjp_bytes(wl.cell, wl.dtype),
@@ -247,12 +281,13 @@ def device_inputs(torch, dev, inp):
 
 
 def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **opts):
-    """Mean wall time of one solve (+ VJP), its iteration count, and the mean duration of the
-    steady-state iteration kernels that did work (HIP events on the launch stream)."""
+    """Mean wall time of one solve (+ VJP) through the plain entry point (fused as opts ask), its
+    iteration count, and the mean duration of the steady-state iteration kernel of one launch per
+    iteration (a few extra solves through the step-wise entry points, HIP events on the launch stream)."""
     stream = torch.cuda.current_stream(out.device)
     recs = []
 
-    def one(record, report=False):
+    def one(record, report=False, hooked=False):
         rec = []
 
         def hook(k, phase):
@@ -262,7 +297,8 @@ def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **
                 rec.append([k, ev, None])
             else:
                 rec[-1][2] = ev
-        _, rep_ = api.newton_solve(cell, pre, w, b, out=out, on_iteration=hook, report=report, **opts)
+        _, rep_ = api.newton_solve(cell, pre, w, b, out=out, on_iteration=hook if hooked else None, report=report,
+                                   **opts)
         if vjp:
             api.scan_vjp(cell, pre, out, g, w, b, want_s0=False, cu_seqlens=opts.get("cu_seqlens"))
         if record:
@@ -274,11 +310,14 @@ def time_solve(torch, api, cell, pre, w, b, g, out, steps, warmup, vjp=False, **
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        one(True)
+        one(False)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     if one(False, report=True) != iters:
         raise RuntimeError("the iteration count changed between solves")
+    for _ in range(3):
+        one(True, hooked=True)
+    torch.cuda.synchronize()
     # steady-state iterations (k >= 1) when there are any: iteration 0 of a zero start reads no iterate
     durs = [e0.elapsed_time(e1) for rec in recs for k, e0, e1 in rec if (1 if iters > 1 else 0) <= k < iters]
     return ms, iters, float(np.mean(durs))

@@ -46,9 +46,11 @@
 extern "C" {
 #endif
 
-#define PARARNN_ABI_VERSION 5
+#define PARARNN_ABI_VERSION 6
 /* upper bound of Newton iterations per call (report.residual holds one more) */
 #define PARARNN_MAX_ITERS 64
+/* most Newton iterations one fused launch runs (pararnn_newton_opts.fuse_iters) */
+#define PARARNN_MAX_FUSE 8
 
 typedef enum {
   PARARNN_OK = 0,
@@ -134,6 +136,20 @@ typedef struct {
                               H^{k+1}_t = f(H^k_{t-1}, x_t) (the scan element's A set to 0) instead
                               of Newton updates (pararnn-torch README, "API overview": Picard
                               iterations warm the first guess); 0..PARARNN_MAX_ITERS             */
+  int32_t fuse_iters;      /* iterations per launch of pararnn_newton_solve (diagonal GRU and LSTM;
+                              the other cells, and solves with Picard sweeps, always use one launch
+                              per iteration).  1: one launch per iteration.  m in 2..PARARNN_MAX_FUSE:
+                              up to m iterations in one launch that reads the gate inputs and the
+                              first iterate once and keeps the trajectory in registers between them.
+                              0: the library's choice (fixed budget: PARARNN_MAX_FUSE; tolerance
+                              mode: K*(T) of pararnn_newton_budget).  The result, the report and
+                              the residuals are the same, bit for bit, for every value.  In
+                              tolerance mode the first launch runs its m iterations without waiting
+                              for the stop rule; when the rule met an earlier one, a second launch
+                              recomputes the trajectory from the first iterate with the right count
+                              (so a solve whose init_guess overlaps s_out uses one launch per
+                              iteration there).  Workspace: one set of look-back words per fused
+                              iteration.                                                          */
 } pararnn_newton_opts;
 
 typedef struct {          /* (host) */
@@ -155,8 +171,12 @@ typedef struct {          /* (host) */
  * per-step replay that writes H^{k+1} in place.
  *   s_out  [S][B][T][D] fp32 output trajectory (H^{iters}).  Must not overlap pre/w/bias/s0.
  *   report (host, nullable): when given, the call waits for the stream and fills it.
+ * Several iterations can share one launch (opts.fuse_iters): the same per-iteration arithmetic, with
+ * the gate inputs read once and the trajectory kept in registers between iterations.
  * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE before any launch; HIP after a failed launch;
  * DIVERGED (tolerance mode, report given) when a max residual is NaN or Inf.
+ * The workspace size depends on opts (fused iterations); opts = NULL gives a size that fits every
+ * option.  Contents need not be preserved between solves.
  * ---------------------------------------------------------------------------------------------- */
 size_t pararnn_newton_workspace_bytes(const pararnn_problem* prob, const pararnn_newton_opts* opts);
 pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_newton_opts* opts,
@@ -164,9 +184,9 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_n
                                     pararnn_report* report);
 
 /* The same solve in three steps, for callers that time, checkpoint or interleave work between
- * iterations.  pararnn_newton_solve(...) is exactly: prepare; iterate k = 0 .. max_iters-1;
- * [final residual]; report.  All share one workspace and stream; `opts` must be the same object
- * contents in every call of one solve.
+ * iterations.  pararnn_newton_solve(...) with fuse_iters = 1 is exactly: prepare; iterate k = 0 ..
+ * max_iters-1; [final residual]; report (with fused launches it returns the same bits).  All share
+ * one workspace and stream; `opts` must be the same object contents in every call of one solve.
  *   prepare  -- clears the workspace's counters and look-back words (one small kernel).
  *   iterate  -- launches iteration k (0 <= k < max_iters): the kernels of one iteration, reading H^k
  *               (init_guess for k = 0, else s_out) and writing H^{k+1} into s_out.  In tolerance mode a kernel

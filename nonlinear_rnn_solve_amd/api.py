@@ -25,7 +25,8 @@ GATES = {0: 2, 1: 3, 2: 4, 3: 4, 4: 3}
 STATE = {0: 1, 1: 1, 2: 2, 3: 4, 4: 1}
 HEAD_GRU = 4
 MAX_ITERS = 64
-ABI_VERSION = 5
+MAX_FUSE = 8          # PARARNN_MAX_FUSE
+ABI_VERSION = 6
 INIT_ZERO, INIT_WARM = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration", -3: "workspace", -4: "HIP error",
           -5: "Newton diverged"}
@@ -55,7 +56,8 @@ class _Problem(ctypes.Structure):
 
 class _Opts(ctypes.Structure):
     _fields_ = [("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("init_guess", ctypes.c_void_p),
-                ("final_residual", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("picard_iters", ctypes.c_int32)]
+                ("final_residual", ctypes.c_int32), ("init_mode", ctypes.c_int32), ("picard_iters", ctypes.c_int32),
+                ("fuse_iters", ctypes.c_int32)]
 
 
 class _Report(ctypes.Structure):
@@ -244,7 +246,7 @@ def _on_device(pos, name):
 @_on_device(1, "pre")
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
                  final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None,
-                 picard_iters=0):
+                 picard_iters=0, fuse_iters=0):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32 (head_gru: w is
@@ -256,6 +258,9 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     cu_seqlens: int32 [n_seqs + 1] offsets of sequences packed along T (every batch row); each sequence
     after the first starts from the zero state.
     picard_iters: the first picard_iters of the iterations are Picard sweeps H_t = f(H_{t-1}, x_t).
+    fuse_iters: iterations per launch (gru / lstm): 1 = one launch per iteration, 2..MAX_FUSE = up to that
+    many in one launch that keeps the trajectory in registers, 0 = the library's choice.  The result is the
+    same bit for bit; only the launches (and the workspace size) change.
     on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
     launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
     entry points prepare / iterate / report, which launch exactly the same kernels.
@@ -273,7 +278,8 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     if init_guess is not None and tuple(init_guess.shape) != (S, B, T, D):
         raise ValueError("init_guess must be [S, B, T, D]")
     opts = _Opts(int(max_iters or 0), float(tol), init_guess.data_ptr() if init_guess is not None else None,
-                 1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO, int(picard_iters))
+                 1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO, int(picard_iters),
+                 int(fuse_iters))
     nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
     ws = _workspace(nbytes, dev, "newton")
     rep = _Report() if report else None

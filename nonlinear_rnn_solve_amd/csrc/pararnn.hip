@@ -33,6 +33,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstddef>
 #include <cstdint>
@@ -510,31 +511,17 @@ DEV Aff<S> shfl_aff(const Aff<S>& m, int src) {
   return r;
 }
 
-template <class Op>
-__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(Op::MINW)))
-void k_tile(const typename Op::Args a) {
-  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS, NA = S * S + S;
+// the tile of a ticket: its position in scan order, channel group, steps and addressing (the NW
+// waves of TS time slices of a workgroup, L steps and V channels per lane)
+template <int NW, int TS, int L, int V, bool REV>
+DEV void tile_setup(const Common& c, uint32_t ticket, Tile& tl) {
   constexpr int LPR = WAVE / TS, TW = LPR * V;
-  constexpr int NSLOT = Op::NSLOT;
-  constexpr bool REV = Op::REVERSE;
-  static_assert(TS == 1 || TS == 2 || TS == 4, "time slices per wave");
-  __shared__ uint32_t sh_ticket;
-  __shared__ float sh_agg[NA][NW][TW];     // aggregate of each wave's TS*L steps
-  __shared__ float sh_carry[S][NW][TW];    // state entering each wave's steps (in scan order)
-  __shared__ float sh_red[NW];
-
-  if (Op::skip(a)) return;  // uniform: decided from values written by earlier launches
-  const Common& c = a.c;
-  if (threadIdx.x == 0)
-    sh_ticket = __hip_atomic_fetch_add(c.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  Tile tl;
   tl.lane = threadIdx.x % WAVE;
   tl.wave = threadIdx.x / WAVE;
   tl.slice = tl.lane / LPR;
   tl.qlane = tl.lane % LPR;
-  tl.p = sh_ticket / static_cast<uint32_t>(c.n_chains);
-  tl.chain = static_cast<int>(sh_ticket % static_cast<uint32_t>(c.n_chains));
+  tl.p = ticket / static_cast<uint32_t>(c.n_chains);
+  tl.chain = static_cast<int>(ticket % static_cast<uint32_t>(c.n_chains));
   tl.chunk = REV ? c.n_chunks - 1 - tl.p : tl.p;
   tl.t_lo = tl.chunk * static_cast<int64_t>(NW * TS * L) + (tl.wave * TS + tl.slice) * L;
   tl.ch0 = static_cast<int64_t>(tl.chain) * TW + tl.qlane * V;
@@ -571,10 +558,39 @@ void k_tile(const typename Op::Args a) {
     const int64_t left = c.T - tl.t_lo;
     tl.nvalid = static_cast<int>(left < 0 ? 0 : (left > L ? L : left));
   }
+}
 
-  typename Op::Lane ln;
-  float rmax = Op::produce(a, tl, ln);
+// the scan's LDS: each wave's aggregate of its TS*L steps, the state entering each wave's steps (in
+// scan order), each wave's max residual
+template <class Op>
+struct TileShm {
+  static constexpr int S = Op::S, NW = Op::NW, TW = (WAVE / Op::TS) * Op::V, NA = S * S + S;
+  float (&agg)[NA][NW][TW];
+  float (&carry)[S][NW][TW];
+  float (&red)[NW];
+};
+// declares the scan's LDS arrays (and the ticket) in a kernel and the view sh of them
+#define PR_TILE_SHM(Op)                                                                           \
+  __shared__ uint32_t sh_ticket;                                                                  \
+  __shared__ float sh_agg_[TileShm<Op>::NA][TileShm<Op>::NW][TileShm<Op>::TW];                    \
+  __shared__ float sh_carry_[TileShm<Op>::S][TileShm<Op>::NW][TileShm<Op>::TW];                   \
+  __shared__ float sh_red_[TileShm<Op>::NW];                                                      \
+  TileShm<Op> sh{sh_agg_, sh_carry_, sh_red_}
 
+// One scan over the tile's elements ln: each lane's aggregate, the wave's slices, the waves through
+// LDS, the look-back across tiles (words of c), and the state entering each lane's steps.  With
+// Op::RESID the tile's max of the lanes' rmax goes to res_slot.  Every thread of the workgroup calls
+// it (two barriers inside).
+template <class Op>
+DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_slot, const Tile& tl,
+                   typename Op::Lane& ln, float rmax, const TileShm<Op>& sh, float (&enter)[Op::V][Op::S]) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS, NA = S * S + S;
+  constexpr int LPR = WAVE / TS, TW = LPR * V;
+  constexpr int NSLOT = Op::NSLOT;
+  constexpr bool REV = Op::REVERSE;
+  auto& sh_agg = sh.agg;
+  auto& sh_carry = sh.carry;
+  auto& sh_red = sh.red;
   // per-lane aggregate over its L steps, in scan order; then across the wave's TS slices
   const int q0 = tl.qlane * V;
   const int sp = REV ? TS - 1 - tl.slice : tl.slice;   // the slice's position in scan order
@@ -614,7 +630,7 @@ void k_tile(const typename Op::Args a) {
       float m = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) m = nanmax(m, sh_red[w]);
-      atomicMax(a.res_slot, __float_as_uint(m));
+      atomicMax(res_slot, __float_as_uint(m));
     }
   }
 
@@ -685,7 +701,6 @@ void k_tile(const typename Op::Args a) {
   __syncthreads();
 
   // state entering this lane's steps: the wave's entering state advanced through earlier slices
-  float x[V][S];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     float xv[S];
@@ -693,8 +708,35 @@ void k_tile(const typename Op::Args a) {
     for (int k = 0; k < S; ++k) xv[k] = sh_carry[k][tl.wave][q0 + v];
     if constexpr (TS > 1) apply(excl[v], xv);
 #pragma unroll
-    for (int k = 0; k < S; ++k) x[v][k] = xv[k];
+    for (int k = 0; k < S; ++k) enter[v][k] = xv[k];
   }
+}
+
+template <class Op>
+DEV uint32_t* op_res_slot(const typename Op::Args& a) {
+  if constexpr (Op::RESID) return a.res_slot;
+  else return nullptr;
+}
+
+template <class Op>
+__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(Op::MINW)))
+void k_tile(const typename Op::Args a) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS;
+  static_assert(TS == 1 || TS == 2 || TS == 4, "time slices per wave");
+  PR_TILE_SHM(Op);
+
+  if (Op::skip(a)) return;  // uniform: decided from values written by earlier launches
+  const Common& c = a.c;
+  if (threadIdx.x == 0)
+    sh_ticket = __hip_atomic_fetch_add(c.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  Tile tl;
+  tile_setup<NW, TS, L, V, Op::REVERSE>(c, sh_ticket, tl);
+
+  typename Op::Lane ln;
+  const float rmax = Op::produce(a, tl, ln);
+  float x[V][S];
+  tile_scan<Op>(a, c, op_res_slot<Op>(a), tl, ln, rmax, sh, x);
   Op::finish(a, tl, ln, x);
 }
 
@@ -986,6 +1028,7 @@ struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = false, RESID = true;
+  static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
   static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
@@ -1041,17 +1084,61 @@ struct NewtonOp {
       for (int k = 0; k < S; ++k) o[k] = q.s2[k];
     }
   }
+  // one lane's inputs of an iteration: the current iterate at steps t_lo-1 .. t_lo+L-1 (h[.][0] is the
+  // step before the lane's first), the gate inputs of its L steps, its channels' parameters and the
+  // packed-sequence start bits of its steps
+  struct Regs {
+    float h[S][L + 1][V];
+    float u[G][L][V];
+    Params<G, V> pm;
+    uint32_t sb;
+  };
+  // a lane's gate inputs as 32-bit words (the fused pass parks them in LDS between iterations): two
+  // bf16 values a word -- exact, since they were read as bf16 -- or one fp32 value
+  static constexpr int UWORDS = DT == DT_BF16 ? (G * L * V + 1) / 2 : G * L * V;
+  static DEV void pack_u(const Regs& rg, uint32_t (&w)[UWORDS]) {
+    const float* u = &rg.u[0][0][0];
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int q = 0; q < UWORDS; ++q) {
+        const uint32_t lo = __float_as_uint(u[2 * q]) >> 16;
+        const uint32_t hi = 2 * q + 1 < G * L * V ? __float_as_uint(u[2 * q + 1]) & 0xffff0000u : 0u;
+        w[q] = hi | lo;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < UWORDS; ++q) w[q] = __float_as_uint(u[q]);
+    }
+  }
+  static DEV void unpack_u(const uint32_t (&w)[UWORDS], Regs& rg) {
+    float* u = &rg.u[0][0][0];
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int q = 0; q < UWORDS; ++q) {
+        u[2 * q] = __uint_as_float(w[q] << 16);
+        if (2 * q + 1 < G * L * V) u[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < UWORDS; ++q) u[q] = __uint_as_float(w[q]);
+    }
+  }
   template <bool MASKED, bool PIC>
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
+    Regs rg;
+    load<MASKED>(a, tl, rg);
+    return elements<MASKED, PIC>(tl, rg, ln);
+  }
+  template <bool MASKED>
+  static DEV void load(const Args& a, const Tile& tl, Regs& rg) {
     const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
     const Common& c = a.c;
     constexpr int TW = (WAVE / TS) * V;
     const int q0 = tl.qlane * V;
     const bool have_h = a.h_in != nullptr;
-    // loads first, all of them: the current iterate at steps t_lo-1 .. t_lo+L-1 (h[.][0] is the
-    // step before the lane's first) and the gate inputs of the lane's L steps
-    float h[S][L + 1][V];
-    float u[G][L][V];
+    // loads first, all of them
+    float (&h)[S][L + 1][V] = rg.h;
+    float (&u)[G][L][V] = rg.u;
     const bool fast = !MASKED && c.off32 && (S == 1 || PR_FAST_S2);   // uniform
     if (have_h && fast) {
       // one descriptor per state plane at the wave's step before its first; step i is i+1 rows on
@@ -1102,7 +1189,7 @@ struct NewtonOp {
         for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], (row + t) * D + tl.d0, u[g][i]);
       }
     }
-    Params<G, V> pm;
+    Params<G, V>& pm = rg.pm;
     if constexpr (CELL != CELL_LINEAR) load_params<CELL, G, V>(a.w, a.bias, D, tl.d0, pm);
     if (!have_h && a.warm) {
       // warm first iterate: every step's state is the cell applied to a zero previous state, so
@@ -1178,13 +1265,20 @@ struct NewtonOp {
     }
     // packed sequences: a step that begins a sequence starts from the zero state, so its previous
     // state is 0 and its Jacobian (the element's A) is zero
-    uint32_t sb = 0;
-    if constexpr (SEG) sb = seg_bits(c.seg, tl.t_lo, T);
+    rg.sb = 0;
+    if constexpr (SEG) rg.sb = seg_bits(c.seg, tl.t_lo, T);
+  }
+  // the scan elements of the lane's steps at the iterate in r, and the max residual over its valid steps
+  template <bool MASKED, bool PIC>
+  static DEV float elements(const Tile& tl, const Regs& rg, Lane& ln) {
+    const float (&h)[S][L + 1][V] = rg.h;
+    const float (&u)[G][L][V] = rg.u;
+    const Params<G, V>& pm = rg.pm;
     ResidMax rm;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const bool ok = !MASKED || i < tl.nvalid;
-      const bool rs = SEG && ((sb >> i) & 1u);
+      const bool rs = SEG && ((rg.sb >> i) & 1u);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         Aff<S> e;
@@ -1247,6 +1341,32 @@ struct NewtonOp {
       }
     }
     return tl.active ? rm.get() : 0.0f;
+  }
+  // the update of finish kept in registers instead of stored: rg.h[.][i+1] becomes H^{k+1} at the
+  // lane's step i (the same multiply-adds in the same order).  Steps past T take the last state: the
+  // next iteration masks them, and writing every register ends the old values' lives here.
+  static DEV void advance(const Tile& tl, const Lane& ln, float (&x)[V][S], Regs& rg) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i < tl.nvalid) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) apply_masked<S, EMASK>(ln.e[v][i], x[v]);
+      }
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) rg.h[k][i + 1][v] = x[v][k];
+    }
+  }
+  // the re-run of a speculative fused pass of m iterations from iteration a.k (tolerance mode): the
+  // iterations the solve really runs from there, j + 1 for the first j < m - 1 whose residual met the
+  // stop rule of skip, or 0 when none did (then the pass's result stands)
+  static DEV int redo_count(const Args& a, int m) {
+    for (int j = 0; j + 1 < m; ++j) {
+      const float r = __uint_as_float(a.res_hist[a.k + j]);
+      if (!(r >= a.tol) || r == INFINITY) return j + 1;
+    }
+    return 0;
   }
   static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
     if (!tl.active) return;
@@ -1534,6 +1654,205 @@ struct VjpOp {
 };
 
 // ------------------------------------------------------------------------------------------------
+// Fused Newton pass: iterations k .. k+m-1 of a tile in one launch (diagonal GRU and LSTM).  The tile
+// loads its gate inputs and the first iterate once and keeps the trajectory in registers from one
+// iteration to the next; only the last iteration writes it.  Each iteration is the element, scan and
+// update arithmetic of one k_tile<NewtonOp> launch, with look-back words of its own (region j).  The
+// state before a lane's first step is the value the lane of the previous segment computed -- by a
+// shuffle within the wave, through LDS across waves, by a halo word across tiles -- which is what
+// k_tile reads back from memory, so the trajectory equals m launches of k_tile bit for bit.
+// Deadlock freedom is k_tile's: tiles take tickets in scan order, and a tile waits only on tiles with
+// smaller tickets, each of which is resident or done.
+// ------------------------------------------------------------------------------------------------
+struct FuseArgs {
+  int32_t m;        // iterations of this launch
+  int32_t redo;     // nonzero: re-run of a speculative pass (NewtonOp::redo_count decides, uniformly)
+  int64_t region;   // look-back words from one iteration's region to the next
+};
+
+// The lane's gate inputs and its channels' parameters back from LDS at the start of every iteration of
+// a fused pass.  The empty asm is a compiler memory barrier (no instruction): the reads are not merged
+// with the stores before the loop, so no value derived from them is hoisted out of it to occupy
+// registers across the scans.
+template <class Op>
+DEV void fused_inputs(const Tile& tl, const uint32_t (*sh_u)[Op::NW * WAVE],
+                      const float (*sh_pm)[4][(WAVE / Op::TS) * Op::V], typename Op::Regs& rg) {
+  constexpr int G = Op::G, V = Op::V;
+  asm volatile("" ::: "memory");
+  uint32_t w[Op::UWORDS];
+#pragma unroll
+  for (int q = 0; q < Op::UWORDS; ++q) w[q] = sh_u[q][threadIdx.x];
+  Op::unpack_u(w, rg);
+  const int q0 = tl.qlane * V;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      rg.pm.w[g][v] = sh_pm[g][0][q0 + v];
+      rg.pm.bias[g][v] = sh_pm[g][1][q0 + v];
+      rg.pm.sw[g][v] = sh_pm[g][2][q0 + v];
+      rg.pm.sb[g][v] = sh_pm[g][3][q0 + v];
+    }
+}
+
+// Before iteration j >= 1 of a fused pass: the state before the lane's first step at the new iterate
+// (chunk 0's first lane keeps s0): the previous slice's last state by a shuffle, the previous wave's
+// through LDS, the previous tile's from its halo word in region c.
+template <class Op>
+DEV void fused_enter(const Common& c, const Tile& tl, const float (*sh_last)[Op::NW][(WAVE / Op::TS) * Op::V],
+                     typename Op::Regs& rg) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, TS = Op::TS;
+  constexpr int LPR = WAVE / TS, TW = LPR * V, NSLOT = Op::NSLOT;
+  const int q0 = tl.qlane * V;
+  float prev[S][V];
+#pragma unroll
+  for (int k = 0; k < S; ++k)
+#pragma unroll
+    for (int v = 0; v < V; ++v) prev[k][v] = __shfl(rg.h[k][L][v], (tl.lane - LPR + WAVE) % WAVE, WAVE);
+  if (tl.slice > 0) {
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+      for (int v = 0; v < V; ++v) rg.h[k][0][v] = prev[k][v];
+  } else if (tl.wave > 0) {
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+      for (int v = 0; v < V; ++v) rg.h[k][0][v] = sh_last[k][tl.wave - 1][q0 + v];
+  } else if (tl.t_lo != 0 && tl.active) {
+    uint64_t wv[V][S];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k) wv[v][k] = ld_word(word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, Op::HALO + k, q0 + v));
+    bool ok = false;
+    while (!ok) {
+      ok = true;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < S; ++k) ok = ok && word_ok(wv[v][k], c.tag);
+      if (!ok) {
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S; ++k)
+            if (!word_ok(wv[v][k], c.tag))
+              wv[v][k] = ld_word(word_at<S, TW, NSLOT>(c, tl.p - 1, tl.chain, Op::HALO + k, q0 + v));
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k) rg.h[k][0][v] = word_val(wv[v][k]);
+  }
+}
+
+// After iteration j < m-1: this lane's last state for the next iteration, to the next tile's first lane
+// (halo word of region j+1, `region` words on from c) and the next wave's first slice (LDS); ends with a
+// barrier so that the LDS values are visible.
+template <class Op>
+DEV void fused_leave(const Common& c, int64_t region, const Tile& tl,
+                     float (*sh_last)[Op::NW][(WAVE / Op::TS) * Op::V], const typename Op::Regs& rg) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, TS = Op::TS;
+  constexpr int LPR = WAVE / TS, TW = LPR * V, NSLOT = Op::NSLOT;
+  const int q0 = tl.qlane * V;
+  if (tl.last_seg && tl.active && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
+    Common cn = c;
+    cn.lb += region;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+        st_word(word_at<S, TW, NSLOT>(cn, tl.p, tl.chain, Op::HALO + k, q0 + v), c.tag, rg.h[k][L][v]);
+  }
+  if (tl.slice == TS - 1) {
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+      for (int v = 0; v < V; ++v) sh_last[k][tl.wave][q0 + v] = rg.h[k][L][v];
+  }
+  __syncthreads();
+}
+
+// waves per SIMD the fused kernel's registers must leave room for (PR_FUSE_MINW exists for tuning
+// builds); the gate inputs wait in LDS between iterations, so the registers are about k_tile's
+#ifndef PR_FUSE_MINW
+#define PR_FUSE_MINW 4
+#endif
+template <class Op>
+__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(PR_FUSE_MINW)))
+void k_fused(const typename Op::Args a, const FuseArgs f) {
+  constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS;
+  constexpr int TW = (WAVE / TS) * V;
+  static_assert(Op::FUSABLE && !Op::REVERSE, "fused Newton pass");
+  PR_TILE_SHM(Op);
+  __shared__ float sh_last[S][NW][TW];   // each wave's state at its last step
+  __shared__ uint32_t sh_u[Op::UWORDS][NW * WAVE];   // each lane's gate inputs (lane-minor: no bank conflicts)
+  __shared__ float sh_pm[Op::G][4][TW];              // the tile's channel parameters (w, bias, sw, sb)
+
+  if (Op::skip(a)) return;   // uniform, as in k_tile
+  int m = f.m;
+  if (f.redo) {
+    m = Op::redo_count(a, f.m);
+    if (m == 0) return;
+  }
+  if (threadIdx.x == 0)
+    sh_ticket = __hip_atomic_fetch_add(a.c.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  Tile tl;
+  tile_setup<NW, TS, L, V, false>(a.c, sh_ticket, tl);
+
+  typename Op::Regs rg;
+  if (tl.nvalid == L) Op::template load<false>(a, tl, rg);
+  else Op::template load<true>(a, tl, rg);
+  {
+    // the gate inputs wait in LDS (each lane its own slots) and are read back at every iteration, the
+    // first included: nothing derived from them stays live in registers across the scan's barriers
+    uint32_t w[Op::UWORDS];
+    Op::pack_u(rg, w);
+#pragma unroll
+    for (int q = 0; q < Op::UWORDS; ++q) sh_u[q][threadIdx.x] = w[q];
+    if (tl.first_seg) {
+      const int q0 = tl.qlane * V;
+#pragma unroll
+      for (int g = 0; g < Op::G; ++g)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          sh_pm[g][0][q0 + v] = rg.pm.w[g][v];
+          sh_pm[g][1][q0 + v] = rg.pm.bias[g][v];
+          sh_pm[g][2][q0 + v] = rg.pm.sw[g][v];
+          sh_pm[g][3][q0 + v] = rg.pm.sb[g][v];
+        }
+    }
+  }
+  __syncthreads();
+
+  // every iteration but the last keeps the trajectory in registers; the last one stores it
+  typename Op::Lane ln;
+  float x[V][S];
+  for (int j = 0; j + 1 < m; ++j) {
+    Common c = a.c;
+    c.lb += j * f.region;
+    fused_inputs<Op>(tl, sh_u, sh_pm, rg);
+    if (j > 0) fused_enter<Op>(c, tl, sh_last, rg);
+    // the masked elements equal the unmasked ones on full lanes (every step valid), so one variant serves
+    const float rmax = Op::template elements<true, false>(tl, rg, ln);
+    tile_scan<Op>(a, c, a.res_slot + j, tl, ln, rmax, sh, x);
+    Op::advance(tl, ln, x, rg);
+    fused_leave<Op>(c, f.region, tl, sh_last, rg);
+  }
+  Common c = a.c;
+  c.lb += (m - 1) * f.region;
+  fused_inputs<Op>(tl, sh_u, sh_pm, rg);
+  if (m > 1) fused_enter<Op>(c, tl, sh_last, rg);
+  const float rmax = Op::template elements<true, false>(tl, rg, ln);
+  tile_scan<Op>(a, c, a.res_slot + (m - 1), tl, ln, rmax, sh, x);
+  Op::finish(a, tl, ln, x);
+}
+
+// ------------------------------------------------------------------------------------------------
 // auxiliary kernels
 // ------------------------------------------------------------------------------------------------
 // zero-fill (used instead of hipMemsetAsync so that the calls stay capturable)
@@ -1698,6 +2017,7 @@ int gate_count(int cell) {
 // [VJP partials]; the mask is (T >> 5) + 2 words (read two at a time by seg_bits)
 constexpr size_t kHeader = 4096;
 constexpr size_t kResOffset = 2048;  // residual slots (uint32 float bits) inside the header
+constexpr int kRedoTicket = PARARNN_MAX_ITERS + 1;   // ticket slot of a fused pass's re-run launch
 
 // bound on the number of packed sequences (offsets are int32 steps)
 constexpr int64_t kMaxSeqs = INT32_MAX - 1;
@@ -1852,19 +2172,21 @@ struct NewtonKernel {
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
-  static size_t ws(const pararnn_problem* pb) { return lb_offset(pb->T) + align256(geo(pb).lb_bytes()); }
-  static pararnn_status prepare(const pararnn_problem* pb, void* ws, hipStream_t st) {
-    const Geo g = geo(pb);
-    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
-    return prepare_ws(ws, pb->T, g.lb_bytes(), pb->cu_seqlens, pb->n_seqs, st);
+  // `regions` look-back word regions: one per iteration of the longest fused pass (1 without fusion)
+  static size_t ws(const pararnn_problem* pb, int regions) {
+    return lb_offset(pb->T) + static_cast<size_t>(regions) * align256(geo(pb).lb_bytes());
   }
-  static pararnn_status iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
-                                void* ws, hipStream_t st) {
+  static pararnn_status prepare(const pararnn_problem* pb, void* ws, int regions, hipStream_t st) {
     const Geo g = geo(pb);
     if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+    return prepare_ws(ws, pb->T, static_cast<size_t>(regions) * align256(g.lb_bytes()), pb->cu_seqlens, pb->n_seqs,
+                      st);
+  }
+  static typename Op::Args args(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
+                                void* ws, const Geo& g, int ticket_slot) {
     uint32_t* res = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kResOffset);
     typename Op::Args a;
-    a.c = make_common(ws, g, pb->B, pb->T, pb->D, k);
+    a.c = make_common(ws, g, pb->B, pb->T, pb->D, ticket_slot);
     a.c.tag = next_tag();
     for (int i = 0; i < 4; ++i) a.pre[i] = pb->pre[i];
     a.w = pb->w;
@@ -1879,7 +2201,31 @@ struct NewtonKernel {
     a.k = k;
     a.tol = op->tol;
     a.B = pb->B;
-    return launch_tile<Op>(a, g, st);
+    return a;
+  }
+  static pararnn_status iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
+                                void* ws, hipStream_t st) {
+    const Geo g = geo(pb);
+    if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+    return launch_tile<Op>(args(pb, op, k, s_out, ws, g, k), g, st);
+  }
+  // iterations k .. k+m-1 in one launch of k_fused (redo: the re-run launch of a speculative pass)
+  static pararnn_status fused(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, int m, bool redo,
+                              float* s_out, void* ws, hipStream_t st) {
+    if constexpr (!Op::FUSABLE) {
+      return PARARNN_ERR_UNSUPPORTED;
+    } else {
+      const Geo g = geo(pb);
+      if (!grid_ok(g)) return PARARNN_ERR_UNSUPPORTED;
+      const typename Op::Args a = args(pb, op, k, s_out, ws, g, redo ? kRedoTicket : k);
+      FuseArgs f;
+      f.m = m;
+      f.redo = redo ? 1 : 0;
+      f.region = static_cast<int64_t>(align256(g.lb_bytes()) / sizeof(uint64_t));
+      const int64_t tiles = g.n_chains * g.n_chunks;
+      hipLaunchKernelGGL(k_fused<Op>, dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
+      return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+    }
   }
   static pararnn_status final_residual(const pararnn_problem* pb, const float* s_out, void* ws, hipStream_t st) {
     uint32_t* res = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kResOffset);
@@ -1895,16 +2241,19 @@ struct NewtonKernel {
 };
 
 struct NewtonEntry {
-  size_t (*ws)(const pararnn_problem*);
-  pararnn_status (*prepare)(const pararnn_problem*, void*, hipStream_t);
+  size_t (*ws)(const pararnn_problem*, int);
+  pararnn_status (*prepare)(const pararnn_problem*, void*, int, hipStream_t);
   pararnn_status (*iterate)(const pararnn_problem*, const pararnn_newton_opts*, int, float*, void*, hipStream_t);
   pararnn_status (*final_residual)(const pararnn_problem*, const float*, void*, hipStream_t);
+  // NULL for cells without a fused pass
+  pararnn_status (*fused)(const pararnn_problem*, const pararnn_newton_opts*, int, int, bool, float*, void*,
+                          hipStream_t);
 };
 
 template <int CELL, int DT, bool SEG>
 NewtonEntry newton_entry() {
   using K = NewtonKernel<CELL, DT, SEG>;
-  return {K::ws, K::prepare, K::iterate, K::final_residual};
+  return {K::ws, K::prepare, K::iterate, K::final_residual, K::Op::FUSABLE ? K::fused : nullptr};
 }
 
 template <int CELL, int DT>
@@ -2083,11 +2432,6 @@ const char* pararnn_status_string(int s) {
   }
 }
 
-size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_newton_opts*) {
-  if (check_problem(pb) != PARARNN_OK) return 0;
-  if (problem_N(pb) == 0) return kHeader;
-  return pick_newton(pb).ws(pb);
-}
 
 namespace {
 // common validation of the Newton entry points; `need_out` checks s_out as well
@@ -2129,6 +2473,24 @@ int budget(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   return auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T);
 }
 
+// Iterations per launch of a solve's fused passes (1: one launch per iteration).  Fixed budget: all
+// K iterations, PARARNN_MAX_FUSE at a time.  Tolerance mode: the first pass runs the measured K*(T)
+// speculatively (a re-run corrects it when the stop came earlier; single launches follow when it
+// came later).  opts->fuse_iters overrides the length; Picard sweeps and the cells without a fused
+// kernel run one launch per iteration.  NULL opts: the longest pass any options can ask for (the
+// workspace size that fits every solve of the problem).
+int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
+  if (!pick_newton(pb).fused) return 1;
+  if (!op) return PARARNN_MAX_FUSE;
+  if (op->picard_iters > 0 || op->fuse_iters == 1) return 1;
+  const int K = budget(pb, op);
+  int m = PARARNN_MAX_FUSE;
+  if (op->fuse_iters > 1) m = op->fuse_iters;
+  else if (op->tol > 0.0f) m = auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T);
+  m = std::min(m, std::min(K, PARARNN_MAX_FUSE));
+  return m < 1 ? 1 : m;
+}
+
 pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
                             bool need_out, void* ws, size_t ws_bytes) {
   pararnn_status rc = check_problem(pb);
@@ -2136,21 +2498,33 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   if (!op || op->max_iters < 0 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
   if (op->init_mode != PARARNN_INIT_ZERO && op->init_mode != PARARNN_INIT_WARM) return PARARNN_ERR_INVALID_ARG;
   if (op->picard_iters < 0 || op->picard_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
+  if (op->fuse_iters < 0 || op->fuse_iters > PARARNN_MAX_FUSE) return PARARNN_ERR_INVALID_ARG;
   if (op->max_iters == 0 && (pb->cell == CELL_SLSTM || pb->cell == CELL_HEAD_GRU))
     return PARARNN_ERR_INVALID_ARG;   // no measured budget
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
-  if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb).ws(pb)) return PARARNN_ERR_WORKSPACE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb).ws(pb, fuse_len(pb, op))) return PARARNN_ERR_WORKSPACE;
   return PARARNN_OK;
 }
+
+bool overlap(const void* p, const void* q, size_t n) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + n && b < a + n;
+}
 }  // namespace
+
+size_t pararnn_newton_workspace_bytes(const pararnn_problem* pb, const pararnn_newton_opts* op) {
+  if (check_problem(pb) != PARARNN_OK) return 0;
+  if (problem_N(pb) == 0) return kHeader;
+  return pick_newton(pb).ws(pb, fuse_len(pb, op));
+}
 
 pararnn_status pararnn_newton_prepare(const pararnn_problem* pb, const pararnn_newton_opts* op, void* ws,
                                       size_t ws_bytes, void* stream) {
   pararnn_status rc = newton_check(pb, op, nullptr, false, ws, ws_bytes);
   if (rc || problem_N(pb) == 0) return rc;
-  return pick_newton(pb).prepare(pb, ws, static_cast<hipStream_t>(stream));
+  return pick_newton(pb).prepare(pb, ws, fuse_len(pb, op), static_cast<hipStream_t>(stream));
 }
 
 pararnn_status pararnn_newton_iterate(const pararnn_problem* pb, const pararnn_newton_opts* op, int k, float* s_out,
@@ -2212,9 +2586,25 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
   if (problem_N(pb) == 0) return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
   const NewtonEntry ne = pick_newton(pb);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = ne.prepare(pb, ws, st);
+  const int m = fuse_len(pb, op);
+  rc = ne.prepare(pb, ws, m, st);
   const int K = budget(pb, op);
-  for (int k = 0; k < K && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+  const size_t traj = static_cast<size_t>(state_size(pb->cell)) * problem_N(pb) * sizeof(float);
+  if (m <= 1 || (op->tol > 0.0f && op->init_guess && overlap(op->init_guess, s_out, traj))) {
+    // one launch per iteration (a speculative pass could not be re-run: s_out overwrites its start)
+    for (int k = 0; k < K && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+  } else if (op->tol > 0.0f) {
+    // speculative pass of m iterations, its re-run if the stop rule met an earlier one, then single
+    // launches that exit at once once the stop rule is met
+    if (rc == PARARNN_OK) rc = ne.fused(pb, op, 0, m, false, s_out, ws, st);
+    if (rc == PARARNN_OK) rc = ne.fused(pb, op, 0, m, true, s_out, ws, st);
+    for (int k = m; k < K && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+  } else {
+    for (int k = 0; k < K && rc == PARARNN_OK; k += m) {
+      const int n = std::min(m, K - k);
+      rc = n == 1 ? ne.iterate(pb, op, k, s_out, ws, st) : ne.fused(pb, op, k, n, false, s_out, ws, st);
+    }
+  }
   if (rc) return rc;
   if (!report && !op->final_residual) return PARARNN_OK;
   return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);

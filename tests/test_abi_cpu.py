@@ -40,13 +40,13 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pararnn.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pararnn_problem),'
                    ' offsetof(pararnn_problem, pre), offsetof(pararnn_problem, s0),'
                    ' offsetof(pararnn_problem, cu_seqlens), offsetof(pararnn_problem, n_seqs),'
                    ' offsetof(pararnn_problem, head_size),'
                    ' sizeof(pararnn_newton_opts),'
                    ' offsetof(pararnn_newton_opts, final_residual), offsetof(pararnn_newton_opts, init_mode),'
-                   ' offsetof(pararnn_newton_opts, picard_iters),'
+                   ' offsetof(pararnn_newton_opts, picard_iters), offsetof(pararnn_newton_opts, fuse_iters),'
                    ' sizeof(pararnn_report),'
                    ' offsetof(pararnn_report, residual)); return 0;}\n')
     exe = tmp_path / "layout"
@@ -55,7 +55,7 @@ def test_struct_layouts_match_header(tmp_path):
     want = [ctypes.sizeof(api._Problem), api._Problem.pre.offset, api._Problem.s0.offset,
             api._Problem.cu_seqlens.offset, api._Problem.n_seqs.offset, api._Problem.head_size.offset,
             ctypes.sizeof(api._Opts), api._Opts.final_residual.offset, api._Opts.init_mode.offset,
-            api._Opts.picard_iters.offset,
+            api._Opts.picard_iters.offset, api._Opts.fuse_iters.offset,
             ctypes.sizeof(api._Report),
             api._Report.residual.offset]
     assert got == want
@@ -95,6 +95,25 @@ def test_workspace_queries(lib):
     assert lib.pararnn_newton_workspace_bytes(ctypes.byref(h), None) == 0
 
 
+def test_workspace_grows_with_fused_iterations(lib):
+    # one set of look-back words per iteration of the longest fused launch; NULL options size for the most
+    p = _problem(B=2, T=4096, D=1024)
+    size = lambda o: lib.pararnn_newton_workspace_bytes(ctypes.byref(p), ctypes.byref(o) if o else None)  # noqa
+    one = size(api._Opts(3, 0.0, None, 0, 0, 0, 1))
+    three = size(api._Opts(3, 0.0, None, 0, 0, 0, 0))     # fixed budget 3: all three in one launch
+    eight = size(api._Opts(10, 0.0, None, 0, 0, 0, 0))    # fixed budget 10: PARARNN_MAX_FUSE at a time
+    assert one < three < eight == size(None)
+    assert (three - one) * 7 == (eight - one) * 2          # the same region size per fused iteration
+    assert size(api._Opts(8, 0.0, None, 0, 0, 0, 4)) == size(api._Opts(4, 0.0, None, 0, 0, 0, 0))
+    # tolerance mode: the first launch runs the measured K*(T) (3 for the GRU at this length)
+    assert size(api._Opts(8, 1e-5, None, 0, 0, 0, 0)) == three
+    # Picard sweeps, and cells without a fused kernel, use one launch per iteration
+    assert size(api._Opts(3, 0.0, None, 0, 0, 1, 0)) == one
+    q = _problem(cell=3, B=2, T=4096, D=1024)
+    sl = lambda o: lib.pararnn_newton_workspace_bytes(ctypes.byref(q), ctypes.byref(o) if o else None)  # noqa
+    assert sl(api._Opts(8, 0.0, None, 0, 0, 0, 0)) == sl(api._Opts(8, 0.0, None, 0, 0, 0, 1)) == sl(None)
+
+
 def test_validation_codes_without_launching(lib):
     opts = api._Opts(3, 0.0, None, 0)
     ws = ctypes.c_void_p(1 << 20)
@@ -116,6 +135,8 @@ def test_validation_codes_without_launching(lib):
     assert solve(_problem(), o=api._Opts(65, 0.0, None, 0)) == -1
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 2)) == -1   # unknown init mode
     assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 0, -1)) == -1   # negative Picard count
+    assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 0, 0, -1)) == -1   # fused iterations out of range
+    assert solve(_problem(), o=api._Opts(3, 0.0, None, 0, 0, 0, api.MAX_FUSE + 1)) == -1
     assert solve(_problem(cell=3), o=api._Opts(0, 0.0, None, 0)) == -1   # sLSTM has no measured budget
     # head-wise block GRU: the head size must divide D; only 16, 32 and 64 are built; no measured budget
     assert solve(_problem(cell=4, head_size=0)) == -1
@@ -151,7 +172,7 @@ def test_validation_codes_without_launching(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.pararnn_status_string(s).decode() != "unknown status"
-    assert lib.pararnn_abi_version() == api.ABI_VERSION == 5
+    assert lib.pararnn_abi_version() == api.ABI_VERSION == 6
 
 
 def test_binding_refuses_cpu_tensors():
