@@ -333,8 +333,12 @@ def variants_bench(torch, dev, args, wl, inp):
     tcu = torch.from_numpy(cu).to(dev)
     tol = wl.tol if wl.tol > 0 else 0.0
     base = dict(max_iters=wl.max_iters, tol=tol)
+    _, rep = api.newton_solve(wl.cell, pre, w, b, out=out, **base)
     variants = [
-        ("zero start (benchmark line)", base),
+        ("zero start, the library's launch length", base),
+        ("zero start, launch length = the previous solve's %d iterations (benchmark line)" % rep.iters,
+         dict(base, fuse_iters=min(rep.iters, api.MAX_FUSE))),
+        ("zero start, one launch per iteration", dict(base, fuse_iters=1)),
         ("warm start", dict(base, warm_start=True)),
         ("measured budget K*(T), zero start", dict(max_iters=None)),
         ("measured budget K*(T), warm start", dict(max_iters=None, warm_start=True)),
