@@ -1029,6 +1029,8 @@ struct NewtonOp {
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
+  // the fused LSTM always takes the masked elements: its unmasked build spilled more registers and ran 3% slower
+  static constexpr bool FUSE_MASKED = CELL == CELL_LSTM;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
   static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
@@ -1776,13 +1778,17 @@ DEV void fused_leave(const Common& c, int64_t region, const Tile& tl,
   __syncthreads();
 }
 
-// waves per SIMD the fused kernel's registers must leave room for (PR_FUSE_MINW exists for tuning
-// builds); the gate inputs wait in LDS between iterations, so the registers are about k_tile's
-#ifndef PR_FUSE_MINW
-#define PR_FUSE_MINW 4
-#endif
+// waves per SIMD the fused kernel's registers must leave room for: four (two workgroups of 8 waves per CU)
+// when the gate inputs parked in LDS leave room for two workgroups in the CU's 160 KB, else two (the
+// fp32 GRU: 96 KB of inputs)
 template <class Op>
-__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(PR_FUSE_MINW)))
+struct FuseMinw {
+  static constexpr int value = Op::UWORDS * Op::NW * WAVE * 4 <= 64 * 1024 ? 4 : 2;
+};
+// MASKED: the launch has lanes whose steps end at T (T not a multiple of the tile's steps); without it every
+// lane takes the unmasked elements, as k_tile's full lanes do
+template <class Op, bool MASKED>
+__global__ __launch_bounds__(Op::NW * WAVE) __attribute__((amdgpu_waves_per_eu(FuseMinw<Op>::value)))
 void k_fused(const typename Op::Args a, const FuseArgs f) {
   constexpr int S = Op::S, V = Op::V, L = Op::L, NW = Op::NW, TS = Op::TS;
   constexpr int TW = (WAVE / TS) * V;
@@ -1805,7 +1811,7 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
   tile_setup<NW, TS, L, V, false>(a.c, sh_ticket, tl);
 
   typename Op::Regs rg;
-  if (tl.nvalid == L) Op::template load<false>(a, tl, rg);
+  if (!MASKED || tl.nvalid == L) Op::template load<false>(a, tl, rg);
   else Op::template load<true>(a, tl, rg);
   {
     // the gate inputs wait in LDS (each lane its own slots) and are read back at every iteration, the
@@ -1837,8 +1843,8 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
     c.lb += j * f.region;
     fused_inputs<Op>(tl, sh_u, sh_pm, rg);
     if (j > 0) fused_enter<Op>(c, tl, sh_last, rg);
-    // the masked elements equal the unmasked ones on full lanes (every step valid), so one variant serves
-    const float rmax = Op::template elements<true, false>(tl, rg, ln);
+    // in a MASKED launch the masked elements serve every lane: on full lanes they equal the unmasked ones
+    const float rmax = Op::template elements<MASKED, false>(tl, rg, ln);
     tile_scan<Op>(a, c, a.res_slot + j, tl, ln, rmax, sh, x);
     Op::advance(tl, ln, x, rg);
     fused_leave<Op>(c, f.region, tl, sh_last, rg);
@@ -1847,7 +1853,7 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
   c.lb += (m - 1) * f.region;
   fused_inputs<Op>(tl, sh_u, sh_pm, rg);
   if (m > 1) fused_enter<Op>(c, tl, sh_last, rg);
-  const float rmax = Op::template elements<true, false>(tl, rg, ln);
+  const float rmax = Op::template elements<MASKED, false>(tl, rg, ln);
   tile_scan<Op>(a, c, a.res_slot + (m - 1), tl, ln, rmax, sh, x);
   Op::finish(a, tl, ln, x);
 }
@@ -2223,7 +2229,13 @@ struct NewtonKernel {
       f.redo = redo ? 1 : 0;
       f.region = static_cast<int64_t>(align256(g.lb_bytes()) / sizeof(uint64_t));
       const int64_t tiles = g.n_chains * g.n_chunks;
-      hipLaunchKernelGGL(k_fused<Op>, dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
+      bool masked = true;
+      if constexpr (!Op::FUSE_MASKED) masked = pb->T % g.CT != 0;
+      if (masked) {
+        hipLaunchKernelGGL((k_fused<Op, true>), dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
+      } else if constexpr (!Op::FUSE_MASKED) {
+        hipLaunchKernelGGL((k_fused<Op, false>), dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
+      }
       return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
     }
   }
