@@ -1112,25 +1112,28 @@ struct NewtonOp {
       for (int q = 0; q < UWORDS; ++q) w[q] = __float_as_uint(u[q]);
     }
   }
-  static DEV void unpack_u(const uint32_t (&w)[UWORDS], Regs& rg) {
-    float* u = &rg.u[0][0][0];
+  // gate input (g, step i, channel slot v) from the packed words of pack_u, word q at w[q]
+  template <class Words>
+  static DEV float unpack_u(const Words& w, int g, int i, int v) {
+    const int f = (g * L + i) * V + v;
     if constexpr (DT == DT_BF16) {
-#pragma unroll
-      for (int q = 0; q < UWORDS; ++q) {
-        u[2 * q] = __uint_as_float(w[q] << 16);
-        if (2 * q + 1 < G * L * V) u[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-      }
+      const uint32_t x = w[f >> 1];
+      return __uint_as_float((f & 1) ? (x & 0xffff0000u) : (x << 16));
     } else {
-#pragma unroll
-      for (int q = 0; q < UWORDS; ++q) u[q] = __uint_as_float(w[q]);
+      return __uint_as_float(w[f]);
     }
   }
   template <bool MASKED, bool PIC>
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
     Regs rg;
     load<MASKED>(a, tl, rg);
-    return elements<MASKED, PIC>(tl, rg, ln);
+    return elements<MASKED, PIC>(tl, rg, ln, RegU{rg});
   }
+  // gate input (g, step i, channel slot v) from the lane's registers
+  struct RegU {
+    const Regs& rg;
+    DEV float operator()(int g, int i, int v) const { return rg.u[g][i][v]; }
+  };
   template <bool MASKED>
   static DEV void load(const Args& a, const Tile& tl, Regs& rg) {
     const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
@@ -1270,36 +1273,41 @@ struct NewtonOp {
     rg.sb = 0;
     if constexpr (SEG) rg.sb = seg_bits(c.seg, tl.t_lo, T);
   }
-  // the scan elements of the lane's steps at the iterate in r, and the max residual over its valid steps
-  template <bool MASKED, bool PIC>
-  static DEV float elements(const Tile& tl, const Regs& rg, Lane& ln) {
+  // the scan elements of the lane's steps at the iterate in rg, and the max residual over its valid steps;
+  // the gate inputs come from uin(g, i, v), fetched step by step
+  template <bool MASKED, bool PIC, class UIn>
+  static DEV float elements(const Tile& tl, const Regs& rg, Lane& ln, const UIn& uin) {
     const float (&h)[S][L + 1][V] = rg.h;
-    const float (&u)[G][L][V] = rg.u;
     const Params<G, V>& pm = rg.pm;
     ResidMax rm;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const bool ok = !MASKED || i < tl.nvalid;
       const bool rs = SEG && ((rg.sb >> i) & 1u);
+      float ui[G][V];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int v = 0; v < V; ++v) ui[g][v] = uin(g, i, v);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         Aff<S> e;
         // a Picard sweep keeps f and drops the Jacobian: the element is (0, f)
         if constexpr (CELL == CELL_LINEAR) {
           const float hp = rs ? 0.0f : h[0][i][v];
-          const float f = fmaf(u[0][i][v], hp, u[1][i][v]);
+          const float f = fmaf(ui[0][v], hp, ui[1][v]);
           if (ok) rm.add(h[0][i + 1][v] - f);
-          e.A[0] = (rs || PIC) ? 0.0f : u[0][i][v];
-          e.b[0] = PIC ? f : u[1][i][v];
+          e.A[0] = (rs || PIC) ? 0.0f : ui[0][v];
+          e.b[0] = PIC ? f : ui[1][v];
         } else if constexpr (CELL == CELL_GRU) {
           const float hp = rs ? 0.0f : h[0][i][v];
-          const GruOut q = gru_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], hp);
+          const GruOut q = gru_eval(pm, v, ui[0][v], ui[1][v], ui[2][v], hp);
           if (ok) rm.add(h[0][i + 1][v] - q.f);
           e.A[0] = (rs || PIC) ? 0.0f : q.J;
           e.b[0] = PIC ? q.f : fmaf(-q.J, hp, q.f);
         } else if constexpr (CELL == CELL_LSTM) {
           const float cp = rs ? 0.0f : h[0][i][v], hp = rs ? 0.0f : h[1][i][v];
-          const LstmPart q = lstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], cp, hp);
+          const LstmPart q = lstm_eval(pm, v, ui[0][v], ui[1][v], ui[2][v], ui[3][v], cp, hp);
           if (ok) {
             rm.add(h[0][i + 1][v] - q.c2);
             rm.add(h[1][i + 1][v] - q.h2);
@@ -1314,7 +1322,7 @@ struct NewtonOp {
           float sp[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) sp[k] = rs ? 0.0f : h[k][i][v];
-          const SlstmPart q = slstm_eval(pm, v, u[0][i][v], u[1][i][v], u[2][i][v], u[3][i][v], sp[0], sp[1],
+          const SlstmPart q = slstm_eval(pm, v, ui[0][v], ui[1][v], ui[2][v], ui[3][v], sp[0], sp[1],
                                          sp[2], sp[3]);
 #pragma unroll
           for (int k = 0; k < 4; ++k)
@@ -1672,19 +1680,25 @@ struct FuseArgs {
   int64_t region;   // look-back words from one iteration's region to the next
 };
 
-// The lane's gate inputs and its channels' parameters back from LDS at the start of every iteration of
-// a fused pass.  The empty asm is a compiler memory barrier (no instruction): the reads are not merged
-// with the stores before the loop, so no value derived from them is hoisted out of it to occupy
+// A lane's gate inputs in LDS (lane-minor words of NewtonOp::pack_u), read where the element loop uses them.
+template <class Op>
+struct LdsU {
+  const uint32_t (*sh_u)[Op::NW * WAVE];
+  struct Col {
+    const uint32_t (*sh_u)[Op::NW * WAVE];
+    DEV uint32_t operator[](int q) const { return sh_u[q][threadIdx.x]; }
+  };
+  DEV float operator()(int g, int i, int v) const { return Op::unpack_u(Col{sh_u}, g, i, v); }
+};
+
+// The lane's channel parameters back from LDS at the start of every iteration of a fused pass.  The empty
+// asm is a compiler memory barrier (no instruction): no read of the parked gate inputs or parameters is
+// merged with the stores before the loop, so no value derived from them is hoisted out of it to occupy
 // registers across the scans.
 template <class Op>
-DEV void fused_inputs(const Tile& tl, const uint32_t (*sh_u)[Op::NW * WAVE],
-                      const float (*sh_pm)[4][(WAVE / Op::TS) * Op::V], typename Op::Regs& rg) {
+DEV void fused_inputs(const Tile& tl, const float (*sh_pm)[4][(WAVE / Op::TS) * Op::V], typename Op::Regs& rg) {
   constexpr int G = Op::G, V = Op::V;
   asm volatile("" ::: "memory");
-  uint32_t w[Op::UWORDS];
-#pragma unroll
-  for (int q = 0; q < Op::UWORDS; ++q) w[q] = sh_u[q][threadIdx.x];
-  Op::unpack_u(w, rg);
   const int q0 = tl.qlane * V;
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -1841,19 +1855,19 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
   for (int j = 0; j + 1 < m; ++j) {
     Common c = a.c;
     c.lb += j * f.region;
-    fused_inputs<Op>(tl, sh_u, sh_pm, rg);
+    fused_inputs<Op>(tl, sh_pm, rg);
     if (j > 0) fused_enter<Op>(c, tl, sh_last, rg);
     // in a MASKED launch the masked elements serve every lane: on full lanes they equal the unmasked ones
-    const float rmax = Op::template elements<MASKED, false>(tl, rg, ln);
+    const float rmax = Op::template elements<MASKED, false>(tl, rg, ln, LdsU<Op>{sh_u});
     tile_scan<Op>(a, c, a.res_slot + j, tl, ln, rmax, sh, x);
     Op::advance(tl, ln, x, rg);
     fused_leave<Op>(c, f.region, tl, sh_last, rg);
   }
   Common c = a.c;
   c.lb += (m - 1) * f.region;
-  fused_inputs<Op>(tl, sh_u, sh_pm, rg);
+  fused_inputs<Op>(tl, sh_pm, rg);
   if (m > 1) fused_enter<Op>(c, tl, sh_last, rg);
-  const float rmax = Op::template elements<MASKED, false>(tl, rg, ln);
+  const float rmax = Op::template elements<MASKED, false>(tl, rg, ln, LdsU<Op>{sh_u});
   tile_scan<Op>(a, c, a.res_slot + (m - 1), tl, ln, rmax, sh, x);
   Op::finish(a, tl, ln, x);
 }
