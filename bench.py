@@ -43,6 +43,8 @@ sys.path.insert(0, ROOT)
 METRIC = "channel-tokens/s per Newton solve (B*T*D*K/s) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X vector fp32 (256 CUs, 2.4 GHz; the packed-fp32 figure)
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops (fma) x 2.4 GHz: what code without packed-fp32 instructions can reach
+VALU_FP32_NONPACKED_TFLOPS = 78.6
 
 # algorithmic flops of one element-iteration of a Newton solve (fma = 2, add / mul / exp2 / rcp = 1):
 #   GRU: cell value and Jacobian 44, scan element (residual, b = f - J h) 3, composition 3, update 2
@@ -245,8 +247,9 @@ def main():
                     "kernel": "k_fused<NewtonOp>: the solve's %d iterations in %d launch(es)"
                               % (iters, -(-iters // fuse[0])),
                     "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops,
-                    "kernel_ms": kern_ms, "bytes_per_elem": fb, "hbm_gbs": fb * N / (kern_ms * 1e-3) / 1e9,
-                    "copy_gbs": copy_gbs(torch, dev)}
+                    "kernel_ms": kern_ms, "peak_nonpacked": VALU_FP32_NONPACKED_TFLOPS,
+                    "frac_nonpacked": achieved / VALU_FP32_NONPACKED_TFLOPS, "bytes_per_elem": fb,
+                    "hbm_gbs": fb * N / (kern_ms * 1e-3) / 1e9, "copy_gbs": copy_gbs(torch, dev)}
     line = {
         "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",

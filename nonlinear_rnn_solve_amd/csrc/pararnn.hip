@@ -1869,7 +1869,11 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
   if (m > 1) fused_enter<Op>(c, tl, sh_last, rg);
   const float rmax = Op::template elements<MASKED, false>(tl, rg, ln, LdsU<Op>{sh_u});
   tile_scan<Op>(a, c, a.res_slot + (m - 1), tl, ln, rmax, sh, x);
-  Op::finish(a, tl, ln, x);
+  // the stores' addressing from the ticket re-read after the loop, so the compiler cannot compute it early
+  // and keep it in registers through every iteration
+  Tile te;
+  tile_setup<NW, TS, L, V, false>(a.c, sh_ticket, te);
+  Op::finish(a, te, ln, x);
 }
 
 // ------------------------------------------------------------------------------------------------
