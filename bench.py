@@ -79,9 +79,15 @@ def vjp_bytes(cell: str, dtype: str) -> int:
 
 
 def source_hash() -> str:
+    """sha256 of the kernel source's code: comments, trailing blanks and empty lines removed, so that a
+    comment edit leaves a counter record valid and any code edit invalidates it."""
     import hashlib
-    with open(os.path.join(ROOT, "nonlinear_rnn_solve_amd", "csrc", "pararnn.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(os.path.join(ROOT, "nonlinear_rnn_solve_amd", "csrc", "pararnn.hip")) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in txt.splitlines()]
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
 
 
 def measured_traffic(key: str):

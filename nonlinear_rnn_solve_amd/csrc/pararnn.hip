@@ -1895,10 +1895,6 @@ __global__ void k_segmask(const int32_t* cu, int64_t n, int64_t T, uint32_t* mas
   if (s > 0 && s < T) atomicOr(mask + (s >> 5), 1u << (s & 31));
 }
 
-// fixed-order reduction of the VJP parameter partials:
-//   out[j][d] = sum over rows r = (b, chunk) of partial[chunk][j][b*D + d]
-// A workgroup owns 64 consecutive outputs; its 16 row groups each add every 16th row, then the 16
-// partial sums are added in row-group order (bitwise reproducible).
 // Parameter gradients from the per-tile partials [n_chunks][npar][B*D] in a fixed order (bitwise
 // reproducible): stage 1 splits the B*n_chunks rows into kRedSlices contiguous slices and sums each
 // slice per output (rows in ascending order within kRedRows interleaved groups, the groups in order);
