@@ -2070,7 +2070,7 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t 
 // minimum waves per SIMD the register allocation must leave room for); the same values instantiate
 // the kernels and size the workspaces.  The PR_* macros exist for tuning builds.
 #ifndef PR_GRU_CFG
-#define PR_GRU_CFG 2, 8, 8, 4, 2
+#define PR_GRU_CFG 1, 16, 8, 4, 2
 #endif
 #ifndef PR_LSTM_CFG
 #define PR_LSTM_CFG 1, 8, 8, 4, 2
