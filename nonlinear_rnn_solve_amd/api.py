@@ -144,8 +144,12 @@ _ws_cache: dict = {}
 
 
 def _workspace(nbytes: int, device, key: str):
-    """A cached device workspace per (device, key); grown on demand, 256-byte aligned by torch."""
-    k = (str(device), key)
+    """A cached device workspace per (device, current stream, key); grown on demand, 256-byte aligned by torch.
+
+    One per stream because the library's calls use their workspace until they finish on their stream: calls on
+    different streams may overlap, and a graph captured on a stream keeps using that stream's buffer (capture
+    on a stream that has already run the same call, so that nothing is allocated during capture)."""
+    k = (str(device), torch.cuda.current_stream(device).cuda_stream, key)
     buf = _ws_cache.get(k)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
