@@ -1029,8 +1029,6 @@ struct NewtonOp {
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = false, RESID = true;
   static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
-  // the fused LSTM always takes the masked elements: its unmasked build spilled more registers and ran 3% slower
-  static constexpr bool FUSE_MASKED = CELL == CELL_LSTM;
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
   static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
@@ -2243,11 +2241,9 @@ struct NewtonKernel {
       f.redo = redo ? 1 : 0;
       f.region = static_cast<int64_t>(align256(g.lb_bytes()) / sizeof(uint64_t));
       const int64_t tiles = g.n_chains * g.n_chunks;
-      bool masked = true;
-      if constexpr (!Op::FUSE_MASKED) masked = pb->T % g.CT != 0;
-      if (masked) {
+      if (pb->T % g.CT != 0) {
         hipLaunchKernelGGL((k_fused<Op, true>), dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
-      } else if constexpr (!Op::FUSE_MASKED) {
+      } else {
         hipLaunchKernelGGL((k_fused<Op, false>), dim3(static_cast<unsigned>(tiles)), dim3(Op::NW * WAVE), 0, st, a, f);
       }
       return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
