@@ -492,10 +492,27 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
 #endif
 }
 
+// max(x, x of another lane) over a DPP lane pattern; rows outside ROWS read 0 (keep x)
+template <int CTRL, int ROWS>
+DEV uint32_t umax_dpp(uint32_t x) {
+  const uint32_t y = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROWS, 0xf, false));
+  return x > y ? x : y;
+}
+// nanmax over the wave of values that are >= 0 or a NaN with the sign bit clear (a max of |r|): their
+// bit patterns order as unsigned integers the way nanmax orders the values (a NaN above +Inf above
+// every finite value), so the wave reduces the bits with integer max.  Lane pairs, quads, half rows
+// and rows of 16 by DPP permutes, then row 0's maximum into row 1, row 2's into row 3 and rows 0-1's
+// into rows 2-3: lane 63 ends with the wave's maximum, which every lane returns.
 DEV float wave_nanmax(float m) {
-#pragma unroll
-  for (int off = WAVE / 2; off > 0; off >>= 1) m = nanmax(m, __shfl_xor(m, off, WAVE));
-  return m;
+  uint32_t x = __float_as_uint(m);
+  x = umax_dpp<0xb1, 0xf>(x);    // quad_perm [1,0,3,2]
+  x = umax_dpp<0x4e, 0xf>(x);    // quad_perm [2,3,0,1]
+  x = umax_dpp<0x141, 0xf>(x);   // row_half_mirror
+  x = umax_dpp<0x140, 0xf>(x);   // row_mirror
+  x = umax_dpp<0x142, 0xa>(x);   // row_bcast:15
+  x = umax_dpp<0x143, 0xc>(x);   // row_bcast:31
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63)));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -602,16 +619,20 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
     for (int s = 1; s < L; ++s) g = Op::compose_elem(ln.e[v][REV ? L - 1 - s : s], g);
     excl[v] = aff_id<S>();
     if constexpr (TS > 1) {
-      // inclusive scan over slices (Hillis-Steele on lanes LPR apart), then shift by one slice
-      Aff<S> inc = g;
+      // inclusive scan over slices (Hillis-Steele on lanes LPR apart), then shift by one slice; with two
+      // slices the first level's operand already is the earlier slice's inclusive value
+      Aff<S> inc = g, prev;
 #pragma unroll
       for (int d = 1; d < TS; d <<= 1) {
         const int src = tl.lane + (REV ? d : -d) * LPR;
         const Aff<S> o = shfl_aff(inc, (src + WAVE) % WAVE);
         if (sp >= d) inc = compose(inc, o);
+        if (TS == 2) prev = o;
       }
-      const int src = tl.lane + (REV ? 1 : -1) * LPR;
-      const Aff<S> prev = shfl_aff(inc, (src + WAVE) % WAVE);
+      if constexpr (TS > 2) {
+        const int src = tl.lane + (REV ? 1 : -1) * LPR;
+        prev = shfl_aff(inc, (src + WAVE) % WAVE);
+      }
       if (sp > 0) excl[v] = prev;
       g = inc;
     }
@@ -627,10 +648,10 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
   __syncthreads();
   if constexpr (Op::RESID) {
     if (threadIdx.x == 0) {
-      float m = 0.0f;
+      uint32_t m = 0u;   // the waves' maxima, >= 0 or NaN: as bits (see wave_nanmax)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) m = nanmax(m, sh_red[w]);
-      atomicMax(res_slot, __float_as_uint(m));
+      for (int w = 0; w < NW; ++w) m = max(m, __float_as_uint(sh_red[w]));
+      atomicMax(res_slot, m);
     }
   }
 
