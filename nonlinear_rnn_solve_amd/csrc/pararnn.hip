@@ -1374,10 +1374,11 @@ struct NewtonOp {
   // the update of finish kept in registers instead of stored: rg.h[.][i+1] becomes H^{k+1} at the
   // lane's step i (the same multiply-adds in the same order).  Steps past T take the last state: the
   // next iteration masks them, and writing every register ends the old values' lives here.
+  template <bool MASKED>
   static DEV void advance(const Tile& tl, const Lane& ln, float (&x)[V][S], Regs& rg) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      if (i < tl.nvalid) {
+      if (!MASKED || i < tl.nvalid) {   // an unmasked launch has every step of every lane
 #pragma unroll
         for (int v = 0; v < V; ++v) apply_masked<S, EMASK>(ln.e[v][i], x[v]);
       }
@@ -1879,7 +1880,7 @@ void k_fused(const typename Op::Args a, const FuseArgs f) {
     // in a MASKED launch the masked elements serve every lane: on full lanes they equal the unmasked ones
     const float rmax = Op::template elements<MASKED, false>(tl, rg, ln, LdsU<Op>{sh_u});
     tile_scan<Op>(a, c, a.res_slot + j, tl, ln, rmax, sh, x);
-    Op::advance(tl, ln, x, rg);
+    Op::template advance<MASKED>(tl, ln, x, rg);
     fused_leave<Op>(c, f.region, tl, sh_last, rg);
   }
   Common c = a.c;
