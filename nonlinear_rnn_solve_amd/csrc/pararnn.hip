@@ -798,6 +798,13 @@ DEV void load_params(const float* w, const float* bias, int64_t D, int64_t d0, P
   }
 }
 
+// the part of gate g's exponent argument that does not depend on the state, scale * (U + b): the cells
+// add sw * h (GRU candidate: sw * r h) to it
+template <int CELL, int G, int V>
+DEV float gate_in(const Params<G, V>& pm, int g, int v, float u) {
+  return fmaf(gate_scale<CELL>(g), u, pm.sb[g][v]);
+}
+
 // sigmoid and tanh of a pre-scaled exponent argument x (see Params)
 DEV float sig_x(float x) { return hw_rcp(1.0f + hw_exp2(x)); }
 DEV float tanh_x(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(x)), 1.0f); }
@@ -809,12 +816,13 @@ DEV float tanh_x(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(x)), 1.0f);
 struct GruOut {
   float f, J, pz, pc, r;
 };
+// the cell from its gates' state-independent arguments a = gate_in(U)
 template <int G, int V>
-DEV GruOut gru_eval(const Params<G, V>& pm, int v, float uz, float ur, float uc, float h) {
+DEV GruOut gru_eval_in(const Params<G, V>& pm, int v, float az, float ar, float ac, float h) {
   GruOut o;
-  const float z = sig_x(fmaf(pm.sw[0][v], h, fmaf(-kLog2e, uz, pm.sb[0][v])));
-  const float r = sig_x(fmaf(pm.sw[1][v], h, fmaf(-kLog2e, ur, pm.sb[1][v])));
-  const float c = tanh_x(fmaf(pm.sw[2][v], r * h, fmaf(2.0f * kLog2e, uc, pm.sb[2][v])));
+  const float z = sig_x(fmaf(pm.sw[0][v], h, az));
+  const float r = sig_x(fmaf(pm.sw[1][v], h, ar));
+  const float c = tanh_x(fmaf(pm.sw[2][v], r * h, ac));
   const float cmh = c - h;
   o.f = fmaf(z, cmh, h);
   const float zz = fmaf(-z, z, z);                    // z (1 - z)
@@ -825,6 +833,11 @@ DEV GruOut gru_eval(const Params<G, V>& pm, int v, float uz, float ur, float uc,
   o.J = fmaf(o.pc * pm.w[2][v], fmaf(h * rr, pm.w[1][v], r), fmaf(o.pz, pm.w[0][v], 1.0f - z));
   return o;
 }
+template <int G, int V>
+DEV GruOut gru_eval(const Params<G, V>& pm, int v, float uz, float ur, float uc, float h) {
+  return gru_eval_in(pm, v, gate_in<CELL_GRU>(pm, 0, v, uz), gate_in<CELL_GRU>(pm, 1, v, ur),
+                     gate_in<CELL_GRU>(pm, 2, v, uc), h);
+}
 
 // LSTM: i, f, o = sig(U + w h + b), g = tanh(U_g + w_g h + b_g), c' = f c + i g, h' = o tanh(c')
 struct LstmPart {
@@ -834,12 +847,12 @@ struct LstmPart {
   float dh_o, kh;         // d h' / d u_o, d h' / d c'
 };
 template <int G, int V>
-DEV LstmPart lstm_eval(const Params<G, V>& pm, int v, float ui, float uf, float uo, float ug, float c, float h) {
+DEV LstmPart lstm_eval_in(const Params<G, V>& pm, int v, float ai, float af, float ao, float ag, float c, float h) {
   LstmPart p;
-  const float ig = sig_x(fmaf(pm.sw[0][v], h, fmaf(-kLog2e, ui, pm.sb[0][v])));
-  const float fg = sig_x(fmaf(pm.sw[1][v], h, fmaf(-kLog2e, uf, pm.sb[1][v])));
-  const float og = sig_x(fmaf(pm.sw[2][v], h, fmaf(-kLog2e, uo, pm.sb[2][v])));
-  const float gg = tanh_x(fmaf(pm.sw[3][v], h, fmaf(2.0f * kLog2e, ug, pm.sb[3][v])));
+  const float ig = sig_x(fmaf(pm.sw[0][v], h, ai));
+  const float fg = sig_x(fmaf(pm.sw[1][v], h, af));
+  const float og = sig_x(fmaf(pm.sw[2][v], h, ao));
+  const float gg = tanh_x(fmaf(pm.sw[3][v], h, ag));
   p.c2 = fmaf(fg, c, ig * gg);
   const float tc = tanh_x(2.0f * kLog2e * p.c2);
   p.h2 = og * tc;
@@ -854,6 +867,11 @@ DEV LstmPart lstm_eval(const Params<G, V>& pm, int v, float ui, float uf, float 
   p.J10 = p.kh * fg;
   p.J11 = fmaf(p.dh_o, pm.w[2][v], p.kh * dc_dh);
   return p;
+}
+template <int G, int V>
+DEV LstmPart lstm_eval(const Params<G, V>& pm, int v, float ui, float uf, float uo, float ug, float c, float h) {
+  return lstm_eval_in(pm, v, gate_in<CELL_LSTM>(pm, 0, v, ui), gate_in<CELL_LSTM>(pm, 1, v, uf),
+                      gate_in<CELL_LSTM>(pm, 2, v, uo), gate_in<CELL_LSTM>(pm, 3, v, ug), c, h);
 }
 
 // sLSTM, diagonal recurrence, state (c, n, m, h), gates z, i, f, o (the published sLSTM with
@@ -1114,33 +1132,53 @@ struct NewtonOp {
     Params<G, V> pm;
     uint32_t sb;
   };
-  // a lane's gate inputs as 32-bit words (the fused pass parks them in LDS between iterations): two
-  // bf16 values a word -- exact, since they were read as bf16 -- or one fp32 value
-  static constexpr int UWORDS = DT == DT_BF16 ? (G * L * V + 1) / 2 : G * L * V;
+  // a lane's gate inputs as 32-bit words (the fused pass parks them in LDS between iterations).  The first
+  // NPRE gates are kept as their state-independent arguments gate_in (fp32, the same single fma the cell
+  // does at every iteration, done once), as far as LDS leaves room for two workgroups per CU: all gates of
+  // fp32 inputs and of the LSTM, the first gate of the bf16 GRU.  The others as read: two bf16 values a
+  // word -- exact, since they were read as bf16 -- or one fp32 value.
+  static constexpr int NPRE = CELL == CELL_GRU ? (DT == DT_BF16 ? 1 : G) : (CELL == CELL_LSTM ? G : 0);
+  static constexpr int NRAW = G - NPRE;
+  static constexpr int PWORDS = NPRE * L * V;
+  static constexpr int UWORDS = PWORDS + (DT == DT_BF16 ? (NRAW * L * V + 1) / 2 : NRAW * L * V);
   static DEV void pack_u(const Regs& rg, uint32_t (&w)[UWORDS]) {
-    const float* u = &rg.u[0][0][0];
+#pragma unroll
+    for (int g = 0; g < NPRE; ++g)
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          w[(g * L + i) * V + v] = __float_as_uint(gate_in<CELL>(rg.pm, g, v, rg.u[g][i][v]));
+    const float* u = &rg.u[NPRE][0][0];
+    constexpr int NR = NRAW * L * V;
     if constexpr (DT == DT_BF16) {
 #pragma unroll
-      for (int q = 0; q < UWORDS; ++q) {
+      for (int q = 0; q < UWORDS - PWORDS; ++q) {
         const uint32_t lo = __float_as_uint(u[2 * q]) >> 16;
-        const uint32_t hi = 2 * q + 1 < G * L * V ? __float_as_uint(u[2 * q + 1]) & 0xffff0000u : 0u;
-        w[q] = hi | lo;
+        const uint32_t hi = 2 * q + 1 < NR ? __float_as_uint(u[2 * q + 1]) & 0xffff0000u : 0u;
+        w[PWORDS + q] = hi | lo;
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < UWORDS; ++q) w[q] = __float_as_uint(u[q]);
+      for (int q = 0; q < NR; ++q) w[PWORDS + q] = __float_as_uint(u[q]);
     }
   }
-  // gate input (g, step i, channel slot v) from the packed words of pack_u, word q at w[q]
+  // gate input (g >= NPRE, step i, channel slot v) from the words of pack_u, word q at w[q]
   template <class Words>
   static DEV float unpack_u(const Words& w, int g, int i, int v) {
-    const int f = (g * L + i) * V + v;
+    const int f = ((g - NPRE) * L + i) * V + v;
     if constexpr (DT == DT_BF16) {
-      const uint32_t x = w[f >> 1];
+      const uint32_t x = w[PWORDS + (f >> 1)];
       return __uint_as_float((f & 1) ? (x & 0xffff0000u) : (x << 16));
     } else {
-      return __uint_as_float(w[f]);
+      return __uint_as_float(w[PWORDS + f]);
     }
+  }
+  // gate_in of gate g at step i, channel slot v from the words of pack_u
+  template <class Words>
+  static DEV float unpack_in(const Words& w, const Params<G, V>& pm, int g, int i, int v) {
+    if (g < NPRE) return __uint_as_float(w[(g * L + i) * V + v]);
+    return gate_in<CELL>(pm, g, v, unpack_u(w, g, i, v));
   }
   template <bool MASKED, bool PIC>
   static DEV float produce_t(const Args& a, const Tile& tl, Lane& ln) {
@@ -1148,10 +1186,11 @@ struct NewtonOp {
     load<MASKED>(a, tl, rg);
     return elements<MASKED, PIC>(tl, rg, ln, RegU{rg});
   }
-  // gate input (g, step i, channel slot v) from the lane's registers
+  // gate input (g, step i, channel slot v) from the lane's registers, and its gate_in
   struct RegU {
     const Regs& rg;
     DEV float operator()(int g, int i, int v) const { return rg.u[g][i][v]; }
+    DEV float in(const Params<G, V>& pm, int g, int i, int v) const { return gate_in<CELL>(pm, g, v, rg.u[g][i][v]); }
   };
   template <bool MASKED>
   static DEV void load(const Args& a, const Tile& tl, Regs& rg) {
@@ -1303,11 +1342,15 @@ struct NewtonOp {
     for (int i = 0; i < L; ++i) {
       const bool ok = !MASKED || i < tl.nvalid;
       const bool rs = SEG && ((rg.sb >> i) & 1u);
+      // the GRU and LSTM take each gate's gate_in, the linear cell and the sLSTM the inputs themselves
       float ui[G][V];
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int v = 0; v < V; ++v) ui[g][v] = uin(g, i, v);
+        for (int v = 0; v < V; ++v) {
+          if constexpr (CELL == CELL_GRU || CELL == CELL_LSTM) ui[g][v] = uin.in(pm, g, i, v);
+          else ui[g][v] = uin(g, i, v);
+        }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         Aff<S> e;
@@ -1320,13 +1363,13 @@ struct NewtonOp {
           e.b[0] = PIC ? f : ui[1][v];
         } else if constexpr (CELL == CELL_GRU) {
           const float hp = rs ? 0.0f : h[0][i][v];
-          const GruOut q = gru_eval(pm, v, ui[0][v], ui[1][v], ui[2][v], hp);
+          const GruOut q = gru_eval_in(pm, v, ui[0][v], ui[1][v], ui[2][v], hp);
           if (ok) rm.add(h[0][i + 1][v] - q.f);
           e.A[0] = (rs || PIC) ? 0.0f : q.J;
           e.b[0] = PIC ? q.f : fmaf(-q.J, hp, q.f);
         } else if constexpr (CELL == CELL_LSTM) {
           const float cp = rs ? 0.0f : h[0][i][v], hp = rs ? 0.0f : h[1][i][v];
-          const LstmPart q = lstm_eval(pm, v, ui[0][v], ui[1][v], ui[2][v], ui[3][v], cp, hp);
+          const LstmPart q = lstm_eval_in(pm, v, ui[0][v], ui[1][v], ui[2][v], ui[3][v], cp, hp);
           if (ok) {
             rm.add(h[0][i + 1][v] - q.c2);
             rm.add(h[1][i + 1][v] - q.h2);
@@ -1709,6 +1752,8 @@ struct LdsU {
     DEV uint32_t operator[](int q) const { return sh_u[q][threadIdx.x]; }
   };
   DEV float operator()(int g, int i, int v) const { return Op::unpack_u(Col{sh_u}, g, i, v); }
+  template <class P>
+  DEV float in(const P& pm, int g, int i, int v) const { return Op::unpack_in(Col{sh_u}, pm, g, i, v); }
 };
 
 // The lane's channel parameters back from LDS at the start of every iteration of a fused pass.  The empty
