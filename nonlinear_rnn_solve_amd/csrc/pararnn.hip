@@ -822,15 +822,16 @@ DEV GruOut gru_eval_in(const Params<G, V>& pm, int v, float az, float ar, float 
   GruOut o;
   const float z = sig_x(fmaf(pm.sw[0][v], h, az));
   const float r = sig_x(fmaf(pm.sw[1][v], h, ar));
-  const float c = tanh_x(fmaf(pm.sw[2][v], r * h, ac));
+  const float rh = r * h;
+  const float c = tanh_x(fmaf(pm.sw[2][v], rh, ac));
   const float cmh = c - h;
   o.f = fmaf(z, cmh, h);
   const float zz = fmaf(-z, z, z);                    // z (1 - z)
-  const float rr = fmaf(-r, r, r);                    // r (1 - r)
+  const float hrr = fmaf(-r, rh, rh);                 // h r (1 - r)
   o.pc = z * fmaf(-c, c, 1.0f);                       // z (1 - c^2)
   o.pz = cmh * zz;
   o.r = r;
-  o.J = fmaf(o.pc * pm.w[2][v], fmaf(h * rr, pm.w[1][v], r), fmaf(o.pz, pm.w[0][v], 1.0f - z));
+  o.J = fmaf(o.pc * pm.w[2][v], fmaf(hrr, pm.w[1][v], r), fmaf(o.pz, pm.w[0][v], 1.0f - z));
   return o;
 }
 template <int G, int V>
