@@ -142,7 +142,8 @@ typedef struct {
                               up to m iterations in one launch that reads the gate inputs and the
                               first iterate once and keeps the trajectory in registers between them.
                               0: the library's choice (fixed budget: PARARNN_MAX_FUSE; tolerance
-                              mode: K*(T) of pararnn_newton_budget).  The result, the report and
+                              mode: K*(T) of pararnn_newton_budget, plus one when tol <= 1e-4, the
+                              bar K*(T) was measured at).  The result, the report and
                               the residuals are the same, bit for bit, for every value.  In
                               tolerance mode the first launch runs its m iterations without waiting
                               for the stop rule; when the rule met an earlier one, a second launch

@@ -2563,12 +2563,19 @@ int budget(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   return auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T);
 }
 
+// the agreement bar of the K*(T) table (max abs against the unroll)
+constexpr float kKStarTau = 1e-4f;
+
 // Iterations per launch of a solve's fused passes (1: one launch per iteration).  Fixed budget: all
-// K iterations, PARARNN_MAX_FUSE at a time.  Tolerance mode: the first pass runs the measured K*(T)
-// speculatively (a re-run corrects it when the stop came earlier; single launches follow when it
-// came later).  opts->fuse_iters overrides the length; Picard sweeps and the cells without a fused
-// kernel run one launch per iteration.  NULL opts: the longest pass any options can ask for (the
-// workspace size that fits every solve of the problem).
+// K iterations, PARARNN_MAX_FUSE at a time.  Tolerance mode: the first pass runs speculatively (a
+// re-run corrects it when the stop came earlier; single launches follow when it came later) for the
+// measured K*(T) iterations, and one more when tol is at or below the table's agreement bar: the
+// residual R_k of an iterate that misses the unroll by 1e-4 or more is itself no smaller, so the stop
+// rule reads R_{K*} at the earliest, in iteration K* + 1 (the fp64 oracle on the table's inputs stops
+// at K* + 1 or K* + 2 for every cell, first iterate and length of the table at tol 1e-4 .. 1e-6).
+// opts->fuse_iters overrides the length; Picard sweeps and the cells without a fused kernel run one
+// launch per iteration.  NULL opts: the longest pass any options can ask for (the workspace size that
+// fits every solve of the problem).
 int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   if (!pick_newton(pb).fused) return 1;
   if (!op) return PARARNN_MAX_FUSE;
@@ -2576,7 +2583,8 @@ int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   const int K = budget(pb, op);
   int m = PARARNN_MAX_FUSE;
   if (op->fuse_iters > 1) m = op->fuse_iters;
-  else if (op->tol > 0.0f) m = auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T);
+  else if (op->tol > 0.0f)
+    m = auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T) + (op->tol <= kKStarTau ? 1 : 0);
   m = std::min(m, std::min(K, PARARNN_MAX_FUSE));
   return m < 1 ? 1 : m;
 }

@@ -105,8 +105,13 @@ def test_workspace_grows_with_fused_iterations(lib):
     assert one < three < eight == size(None)
     assert (three - one) * 7 == (eight - one) * 2          # the same region size per fused iteration
     assert size(api._Opts(8, 0.0, None, 0, 0, 0, 4)) == size(api._Opts(4, 0.0, None, 0, 0, 0, 0))
-    # tolerance mode: the first launch runs the measured K*(T) (3 for the GRU at this length)
-    assert size(api._Opts(8, 1e-5, None, 0, 0, 0, 0)) == three
+    # tolerance mode: the first launch runs the measured K*(T) (3 for the GRU at this length), one more when
+    # tol is at or below the 1e-4 bar K*(T) was measured at
+    four = size(api._Opts(4, 0.0, None, 0, 0, 0, 0))
+    assert (four - one) * 2 == (three - one) * 3
+    assert size(api._Opts(8, 1e-3, None, 0, 0, 0, 0)) == three
+    assert size(api._Opts(8, 1e-4, None, 0, 0, 0, 0)) == size(api._Opts(8, 1e-5, None, 0, 0, 0, 0)) == four
+    assert size(api._Opts(3, 1e-5, None, 0, 0, 0, 0)) == three        # never beyond the budget
     # Picard sweeps, and cells without a fused kernel, use one launch per iteration
     assert size(api._Opts(3, 0.0, None, 0, 0, 1, 0)) == one
     q = _problem(cell=3, B=2, T=4096, D=1024)
