@@ -325,6 +325,12 @@ def test_full_config4_newton_tol_and_vjp():
     got, rep = api.newton_solve("gru", pre, w, b, max_iters=wl.max_iters, tol=wl.tol, final_residual=True)
     print("  iters", rep.iters, rep.residuals)
     assert rep.converged and rep.final_residual < wl.tol
+    # the launch configuration the benchmark times (the solve's iteration count in one fused launch): the
+    # same bits and the same report as the library's default launch length checked below
+    got_b, rep_b = api.newton_solve("gru", pre, w, b, max_iters=wl.max_iters, tol=wl.tol, final_residual=True,
+                                    fuse_iters=rep.iters)
+    assert torch.equal(got_b, got) and rep_b.iters == rep.iters and rep_b.residuals == rep.residuals
+    del got_b
     ch = sample_channels(wl.B, wl.D, 16, seed=3)
     prob = oracle_problem(inp, channels=ch)
     H = oracle.newton(prob, rep.iters)[0]
