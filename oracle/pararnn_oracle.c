@@ -438,6 +438,16 @@ int or_residual(const or_problem* p, const double* H, double* out_max, int nthre
  * below tol is the last one; its update is still applied (the fused GPU pass
  * evaluates the residual and produces the update in one sweep).  A
  * non-finite R_k stops the loop and reports divergence.
+ * A grown residual is divergence too (a reading: the README, "Evaluation",
+ * has a divergence error carry the residual history and states no rule): with
+ * tol > 0, a solve that spends its whole budget without meeting tol and whose
+ * last residual R_{K-1} exceeds R_{k0}, the residual of the iterate Newton
+ * started from (k0 = the number of Picard sweeps before it), ends worse than
+ * it began.  Growth from one iteration to the next is not judged on its own:
+ * on this triangular system Newton is exact after T updates, and on the
+ * benchmark distributions the max residual of a solve that converges can
+ * rise for a few iterations first (the LSTM's first update at long T, the
+ * sLSTM's first Newton updates after its Picard sweeps).
  * Output: H^{iters}; resid[0..iters-1] = R_0..R_{iters-1}.
  */
 
@@ -556,6 +566,9 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int p
     if (!isfinite(R)) { status = OR_DIVERGED; break; } /* NaN or Inf */
     if (tol > 0.0 && R < tol) { conv = 1; break; }
   }
+  /* the budget spent without convergence, ending above the residual Newton started from */
+  if (status == OR_OK && tol > 0.0 && !conv && k_done - 1 > picard_iters && resid[k_done - 1] > resid[picard_iters])
+    status = OR_DIVERGED;
   free(wm);
   free(scratch);
   *iters = k_done;
@@ -1009,6 +1022,9 @@ static int hgru_newton(const or_problem* p, double* Hv, int picard_iters, int ma
     if (!isfinite(R)) { status = OR_DIVERGED; break; }
     if (tol > 0.0 && R < tol) { conv = 1; break; }
   }
+  /* the budget spent without convergence, ending above the residual Newton started from (or_newton) */
+  if (status == OR_OK && tol > 0.0 && !conv && k_done - 1 > picard_iters && resid[k_done - 1] > resid[picard_iters])
+    status = OR_DIVERGED;
   free(wm);
   *iters = k_done;
   *converged = conv;
