@@ -14,18 +14,25 @@ automatic budget over a grid of sequence lengths; --slstm and --head time the di
 head-wise block GRU.  None of them is the benchmark line.
 
 Prints ONE JSON line.  value = channel-tokens/s = B*T*D*K / (seconds per step), K the Newton
-iterations the solve ran (a linear scan counts K = 1).  The solve runs its iterations fused: one
-launch that reads the gate inputs once and keeps the trajectory in registers (fuse_iters = the
-iteration count of the untimed solve before the timed region, as a loop of solves would speculate;
-the result is the same bit for bit for any value).  roofline: that launch is bound by vector ALU
-issue, so it is rated in algorithmic flops (flops per element-iteration of the cell, its scan element,
-composition and update, as the kernel's arithmetic is written: fma = 2, add / mul / exp2 / rcp = 1) x
-elements x iterations / the solve's duration from HIP events on the launch stream (the fused launch
-plus the solve's empty launches), against the fp32 vector peak; for the linear scan, HBM bytes as
-before.  roofline.copy_gbs is a device-to-device copy's bandwidth on the same GPU, for context;
-per_iteration_kernel is the one-launch-per-iteration kernel's HBM figure, timed after the timed
-region.  cpu_baseline: the fp64 CPU oracle on a bounded sample of channels of the same workload
-(value: its Newton solve + VJP; unroll_value: its sequential unroll, the exact solution).
+iterations the solve ran (a linear scan counts K = 1).  The timed solves use the library's own launch
+length (fuse_iters = 0: in tolerance mode a speculative fused launch of K*(T) + 1 iterations, its
+re-run launch, then one launch per further iteration).  fuse_prev times the same step with the launch
+length set to the iteration count of the solve before it (a loop of solves can pass that; the result is
+the same bit for bit), for context only.
+
+roofline: HBM, as the method's bytes: a Newton iteration reads the gate inputs and H^k and writes
+H^{k+1} (GRU bf16: 6 + 4 + 4 = 14 B per element; iteration 0 of a zero start reads no H^k: 10 B;
+LSTM fp32: 16 + 8 + 8 = 32, 24), the linear scan reads a, b and writes h (12 B).  achieved = those
+bytes for the iterations the solve ran x elements / the duration of the solve's launches (HIP events on
+the launch stream around every solve of the timed region).  The fused launch keeps the trajectory on
+chip between iterations, so its effective rate can exceed what it moves: its real HBM bytes are
+roofline.traffic (rocprofv3 counters, when taken on this source), and roofline.alu rates the same time
+in algorithmic flops (fma = 2, add / mul / exp2 / rcp = 1) against the 78.6 TFLOP/s vector fp32 peak
+that code without packed-fp32 instructions can reach.  roofline.copy_gbs is a device-to-device copy's
+bandwidth on the same GPU, for context; per_iteration_kernel is the one-launch-per-iteration kernel's
+HBM figure, timed after the timed region.  cpu_baseline: the fp64 CPU oracle on a bounded sample of
+channels of the same workload on every core this process may use (value: its Newton solve + VJP;
+unroll_value: its sequential unroll, the exact solution; nproc: the host's core count).
 """
 from __future__ import annotations
 
@@ -46,17 +53,24 @@ VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X vector fp32 (256 CUs, 2.4 GHz; the pack
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flops (fma) x 2.4 GHz: what code without packed-fp32 instructions can reach
 VALU_FP32_NONPACKED_TFLOPS = 78.6
 
+
+def iteration_bytes(cell: str, dtype: str, first: bool) -> int:
+    """HBM bytes per element of one Newton iteration: the gate inputs, H^k (not for iteration 0 of a zero
+    start) and H^{k+1}."""
+    esz = 2 if dtype == "bf16" else 4
+    G, S = (3, 1) if cell == "gru" else (4, 2)
+    return G * esz + (0 if first else 4 * S) + 4 * S
+
+
+def solve_bytes(cell: str, dtype: str, iters: int) -> int:
+    """HBM bytes per element of a zero-start solve of `iters` iterations, iteration by iteration."""
+    return iteration_bytes(cell, dtype, True) + (iters - 1) * iteration_bytes(cell, dtype, False)
+
 # algorithmic flops of one element-iteration of a Newton solve (fma = 2, add / mul / exp2 / rcp = 1):
 #   GRU: cell value and Jacobian 44, scan element (residual, b = f - J h) 3, composition 3, update 2
 #   LSTM: cell 64, elements 10, 2x2 composition 20, update 8
 FLOPS_PER_ELEM_ITER = {"gru": 52, "lstm": 102}
 
-
-def fused_bytes(cell: str, dtype: str) -> int:
-    """HBM bytes per element of a fused solve from the zero start: the gate inputs once, H written once."""
-    esz = 2 if dtype == "bf16" else 4
-    G, S = (3, 1) if cell == "gru" else (4, 2)
-    return G * esz + S * 4
 
 # algorithmic HBM bytes per element of one launch of the dominant kernel
 #   GRU steady iteration: read U (3 planes) + read H^k + write H^{k+1}
@@ -107,12 +121,11 @@ def measured_traffic(key: str):
 
 
 def cpu_threads() -> int:
-    n = os.cpu_count() or 1
+    """Every core this process may run on (its CPU affinity), for the oracle's worker threads."""
     try:
-        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
-    except ValueError:
-        pass
-    return max(1, min(n, 16))
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
 
 
 def main():
@@ -211,15 +224,10 @@ def main():
             iter_events.append(rec)
         return iters
 
-    fuse = [0]   # the library's choice until a solve has reported its iteration count
+    fuse = [0]   # the library's own launch length
     for _ in range(args.warmup):
         step(False)
     iters = step(False, report=True)
-    if wl.cell != "linear":
-        fuse[0] = min(iters, api.MAX_FUSE)
-        step(False)
-        if step(False, report=True) != iters:
-            raise RuntimeError("the iteration count changed with the fused launch length")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -230,7 +238,7 @@ def main():
     if step(False, report=True) != iters:
         raise RuntimeError("the iteration count changed between steps")
 
-    # dominant kernel: the fused Newton launch (the solve's launches, timed together), or the scan
+    # the solve's launches (or the scan), timed by HIP events on the launch stream in every timed step
     kern_ms = float(np.mean([e0.elapsed_time(e1) for rec in iter_events for k, e0, e1 in rec]))
     value = N * iters / (ms_per_step * 1e-3)
     traffic = measured_traffic(wl.name)
@@ -244,35 +252,58 @@ def main():
                     "bytes_per_elem": per_elem, "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
                     "copy_gbs": copy_gbs(torch, dev)}
     else:
-        config["fuse_iters"] = fuse[0]
+        config["fuse_iters"] = 0
+        per_elem = solve_bytes(wl.cell, wl.dtype, iters)
+        achieved = per_elem * N / (kern_ms * 1e-3) / 1e9
         flops = FLOPS_PER_ELEM_ITER[wl.cell] * N * iters
-        achieved = flops / (kern_ms * 1e-3) / 1e12
-        fb = fused_bytes(wl.cell, wl.dtype)
-        roofline = {"bound": "alu", "achieved": achieved, "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / VALU_FP32_PEAK_TFLOPS, "traffic": traffic,
-                    "kernel": "k_fused<NewtonOp>: the solve's %d iterations in %d launch(es)"
-                              % (iters, -(-iters // fuse[0])),
-                    "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops,
-                    "kernel_ms": kern_ms, "peak_nonpacked": VALU_FP32_NONPACKED_TFLOPS,
-                    "frac_nonpacked": achieved / VALU_FP32_NONPACKED_TFLOPS, "bytes_per_elem": fb,
-                    "hbm_gbs": fb * N / (kern_ms * 1e-3) / 1e9, "copy_gbs": copy_gbs(torch, dev)}
+        tflops = flops / (kern_ms * 1e-3) / 1e12
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                    "kernel": "the Newton solve's launches (k_fused<NewtonOp> over the speculated iterations, "
+                              "its re-run launch, k_tile<NewtonOp> for each further one)",
+                    "bytes_per_elem": per_elem,
+                    "bytes_per_elem_note": "%d iterations: %d B for iteration 0 (no H^0 read) + %d B per later one"
+                                           % (iters, iteration_bytes(wl.cell, wl.dtype, True),
+                                              iteration_bytes(wl.cell, wl.dtype, False)),
+                    "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
+                    "alu": {"achieved": tflops, "peak": VALU_FP32_NONPACKED_TFLOPS, "unit": "TFLOP/s",
+                            "frac": tflops / VALU_FP32_NONPACKED_TFLOPS,
+                            "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops},
+                    "copy_gbs": copy_gbs(torch, dev)}
     line = {
         "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": config, "roofline": roofline,
     }
-    if wl.cell != "linear":
-        # the one-launch-per-iteration kernel (steady iterations k >= 1), timed after the timed region
-        _, _, it_ms = time_solve(torch, api, wl.cell, pre, w, b, g, out, 1, 1, max_iters=wl.max_iters,
-                                 tol=wl.tol, fuse_iters=1)
-        per_elem = algo_bytes(wl.cell, wl.dtype)
-        gbs = per_elem * N / (it_ms * 1e-3) / 1e9
-        line["per_iteration_kernel"] = {"kernel": "k_tile<NewtonOp> (iterations k>=1, fuse_iters=1)", "ms": it_ms,
-                                        "bytes_per_elem": per_elem, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     if vjp_events:
         vms = float(np.mean([a.elapsed_time(b2) for a, b2 in vjp_events]))
         line["vjp"] = {"ms": vms, "bytes_per_elem": vjp_bytes(wl.cell, wl.dtype),
-                       "gbs": vjp_bytes(wl.cell, wl.dtype) * N / (vms * 1e-3) / 1e9}
+                       "gbs": vjp_bytes(wl.cell, wl.dtype) * N / (vms * 1e-3) / 1e9,
+                       "frac_hbm": vjp_bytes(wl.cell, wl.dtype) * N / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if wl.cell != "linear":
+        # context, after the timed region: the same step with the launch length set to the previous solve's
+        # iteration count (one fused launch for the whole solve), and the one-launch-per-iteration kernel
+        fuse[0] = min(iters, api.MAX_FUSE)
+        if step(False, report=True) != iters:
+            raise RuntimeError("the iteration count changed with the fused launch length")
+        iter_events.clear()
+        vjp_events.clear()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        pm = (time.perf_counter() - t0) * 1e3 / args.steps
+        pk = float(np.mean([e0.elapsed_time(e1) for rec in iter_events for k, e0, e1 in rec]))
+        line["fuse_prev"] = {"fuse_iters": fuse[0], "ms_per_step": pm, "value": N * iters / (pm * 1e-3),
+                             "solve_ms": pk, "gbs": per_elem * N / (pk * 1e-3) / 1e9,
+                             "frac_hbm": per_elem * N / (pk * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        _, _, it_ms = time_solve(torch, api, wl.cell, pre, w, b, g, out, 1, 1, max_iters=wl.max_iters,
+                                 tol=wl.tol, fuse_iters=1)
+        pe = algo_bytes(wl.cell, wl.dtype)
+        gbs = pe * N / (it_ms * 1e-3) / 1e9
+        line["per_iteration_kernel"] = {"kernel": "k_tile<NewtonOp> (iterations k>=1, fuse_iters=1)", "ms": it_ms,
+                                        "bytes_per_elem": pe, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp, iters, args.cpu_channels)
     print(json.dumps(line), flush=True)
@@ -551,8 +582,8 @@ def cpu_baseline(wl, inp, iters, n_channels):
     else:
         oracle.unroll(prob, nthreads=threads)
     usec = time.perf_counter() - t1
-    return {"value": n * k / sec, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
-            "unroll_value": n / usec,
+    return {"value": n * k / sec, "unit": "channel-tokens/s", "cores": threads, "nproc": os.cpu_count(),
+            "kind": "oracle", "unroll_value": n / usec,
             "sample": "%d of %d channels, full T=%d, %s%s; %.1f s" % (
                 len(pick), wl.B * wl.D, wl.T, "linear scan" if wl.cell == "linear" else
                 "Newton (%d iterations)" % k, " + VJP" if wl.vjp else "", sec)}

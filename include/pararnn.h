@@ -9,8 +9,8 @@
  * few Newton iterations; each iteration's linearised system
  *     delta_t = J_t delta_{t-1} - r_t,   r_t = h_t - f(h_{t-1}, x_t),
  *     J_t = d f / d h (h_{t-1}, x_t)
- * is a first-order linear recurrence and is solved by an associative scan
- * over time.  The backward pass (same page, "Method") is the adjoint: a
+ * is a first-order linear recurrence, solved here by a parallel scan along
+ * time.  The backward pass (same page, "Method") is the adjoint: a
  * reverse linear recurrence with transposed Jacobians.
  *
  * Conventions for every entry point
@@ -58,7 +58,9 @@ typedef enum {
   PARARNN_ERR_UNSUPPORTED = -2,  /* valid but not built: D not a multiple of 2, or too large a grid */
   PARARNN_ERR_WORKSPACE = -3,    /* ws NULL/misaligned or ws_bytes below the queried size */
   PARARNN_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
-  PARARNN_ERR_DIVERGED = -5      /* tolerance mode saw a non-finite max residual (report still filled) */
+  PARARNN_ERR_DIVERGED = -5      /* tolerance mode: a non-finite max residual, or the budget spent without
+                                    convergence and the last residual above the starting one (see tol);
+                                    the report is still filled */
 } pararnn_status;
 
 typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
@@ -127,7 +129,14 @@ typedef struct {
   float tol;               /* <= 0: run exactly max_iters iterations.
                               > 0: iteration k evaluates R_k = max|r(H^k)| over b, t, d and state
                               components; the first iteration with R_k < tol is the last one (its
-                              update is applied).  A non-finite R_k stops the solve (DIVERGED).     */
+                              update is applied).  A non-finite R_k stops the solve (DIVERGED).  A
+                              solve that spends its budget without convergence and whose last R
+                              exceeds R_{k0}, the residual at the first Newton (not Picard) iteration
+                              k0 = picard_iters, has diverged too (DIVERGED; pararnn-torch README,
+                              "Evaluation": a divergence error with the residual history).  A rise
+                              from one iteration to the next alone is not divergence: on this
+                              triangular system Newton is exact after T updates, and converging LSTM
+                              and sLSTM solves show a few rising iterations first.                 */
   const float* init_guess; /* [S][B][T][D] first iterate H^0, or NULL (then init_mode decides).  May
                               equal s_out (resume from a previous solve's output).                  */
   int32_t final_residual;  /* nonzero: one extra pass computes max|r| of the returned trajectory   */
@@ -175,7 +184,10 @@ typedef struct {          /* (host) */
  * Several iterations can share one launch (opts.fuse_iters): the same per-iteration arithmetic, with
  * the gate inputs read once and the trajectory kept in registers between iterations.
  * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE before any launch; HIP after a failed launch;
- * DIVERGED (tolerance mode, report given) when a max residual is NaN or Inf.
+ * DIVERGED (tolerance mode, report given) when a max residual is NaN or Inf, or when the budget ran out
+ * above the starting residual (see tol).  Without a report the call only launches and returns OK; the
+ * status is then available, after the stream has completed, from pararnn_newton_report on the same
+ * workspace (with final_residual = 0 it launches nothing and reads the residual history the solve left).
  * The workspace size depends on opts (fused iterations); opts = NULL gives a size that fits every
  * option.  Contents need not be preserved between solves.
  * ---------------------------------------------------------------------------------------------- */
@@ -204,7 +216,7 @@ pararnn_status pararnn_newton_report(const pararnn_problem* prob, const pararnn_
 
 /* ------------------------------------------------------------------------------------------------
  * pararnn_linear_scan -- the linear recurrence every Newton step reduces to (pararnn-torch README,
- * "Method": each linear solve is an associative scan over time), as a single-pass parallel scan.
+ * "Method": the linearised system is solved by a parallel scan along time), as a single-pass scan.
  *   forward (reverse = 0): s_{-1} = s0,  s_t = A_t s_{t-1} + b_t,  t = 0 .. T-1
  *   reverse (reverse = 1): s_T    = s0,  s_t = A_t s_{t+1} + b_t,  t = T-1 .. 0
  *   S = 1: a [B][T][D], b [B][T][D];  S = 2: a [4][B][T][D] (A00, A01, A10, A11), b [2][B][T][D].

@@ -10,6 +10,7 @@ the adjoint (reverse scan) for gradients.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import functools
 import os
@@ -39,7 +40,8 @@ class PararnnError(RuntimeError):
 
 
 class NewtonDivergenceError(PararnnError):
-    """Raised when a tolerance-mode solve sees a non-finite max residual; carries the history."""
+    """Raised when a tolerance-mode solve sees a non-finite max residual, or spends its budget without
+    converging and ends above the residual Newton started from; carries the history."""
 
     def __init__(self, status, what, report):
         super().__init__(status, what)
@@ -74,22 +76,37 @@ class NewtonReport:
     final_residual: float | None = None
 
 
-_lib = None
+_libs: dict = {}
+_active = _LIB_PATH
+STRESS_LIB_PATH = os.path.join(_HERE, "libpararnn_stress.so")
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    return _active
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Route the calls made inside the block to the library at `path` (the look-back stress build,
+    libpararnn_stress.so, in the tests); the default library afterwards."""
+    global _active
+    old = _active
+    _active = path
+    try:
+        yield load_library()
+    finally:
+        _active = old
 
 
 def load_library():
     """Load libpararnn.so (built by ``python -m nonlinear_rnn_solve_amd.build``); raises if absent."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError("libpararnn.so not built: run `python -m nonlinear_rnn_solve_amd.build` "
-                           "(there is no CPU fallback)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = _libs.get(_active)
+    if lib is not None:
+        return lib
+    if not os.path.exists(_active):
+        raise RuntimeError("%s not built: run `python -m nonlinear_rnn_solve_amd.build` "
+                           "(there is no CPU fallback)" % os.path.basename(_active))
+    lib = ctypes.CDLL(_active)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.pararnn_abi_version.restype = i32
     lib.pararnn_status_string.restype = ctypes.c_char_p
@@ -114,10 +131,24 @@ def load_library():
     lib.pararnn_vjp_workspace_bytes.argtypes = [vp]
     lib.pararnn_scan_vjp.restype = i32
     lib.pararnn_scan_vjp.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    if hasattr(lib, "pararnn_debug_lookback_depth"):
+        lib.pararnn_debug_lookback_depth.restype = i32
+        lib.pararnn_debug_lookback_depth.argtypes = [i32]
     if lib.pararnn_abi_version() != ABI_VERSION:
-        raise RuntimeError("libpararnn.so ABI mismatch")
-    _lib = lib
+        raise RuntimeError("%s ABI mismatch" % os.path.basename(_active))
+    _libs[_active] = lib
     return lib
+
+
+def lookback_depth(reset=True) -> int:
+    """(stress build only) the deepest look-back walk since the last reset, in aggregates passed."""
+    lib = load_library()
+    if not hasattr(lib, "pararnn_debug_lookback_depth"):
+        raise RuntimeError("%s is not the look-back stress build" % os.path.basename(_active))
+    d = lib.pararnn_debug_lookback_depth(1 if reset else 0)
+    if d < 0:
+        raise PararnnError(d, "pararnn_debug_lookback_depth")
+    return d
 
 
 def _ptr(t):

@@ -40,6 +40,7 @@
 #include <cstring>
 
 #include "pararnn.h"
+#include "pararnn_debug.h"
 
 #define DEV __device__ __forceinline__
 
@@ -355,26 +356,48 @@ DEV uint64_t* word_at(const Common& c, int64_t p, int chain, int slot, int q) {
   return c.lb + ((p * c.n_chains + chain) * NSLOT + slot) * static_cast<int64_t>(TW) + q;
 }
 
-// The state entering position p in scan order, for the V channels of one lane.  The words of
-// positions p-1, p-2, ... are read in windows of W; an inclusive word (the state at the end of
-// that chunk) ends the walk, an aggregate word (the chunk's affine map) extends it.  Position 0
-// publishes its inclusive word without waiting, so the walk always ends.
-#ifndef PR_LB_JOINT
-#define PR_LB_JOINT 1
+// Debug builds (-DPR_LB_STRESS=1) pause the tiles that publish look-back words for a pseudo-random time,
+// different for every launch, tile and call site, so that the words appear in a scrambled order and walks
+// reach far back; the library built so must give the same bits as the plain one.  Every pause is bounded.
+#ifndef PR_LB_STRESS
+#define PR_LB_STRESS 0
 #endif
+#if PR_LB_STRESS
+__device__ uint32_t g_lb_max_depth;   // deepest walk seen: aggregates applied before an inclusive word
+#endif
+DEV void stress_pause(const Common& c, int64_t p, int chain, uint32_t site) {
+  if constexpr (PR_LB_STRESS) {
+    // the tag and the word region (a fused pass's iterations each have their own) seed the pauses
+    const uint32_t tag = c.tag ^ static_cast<uint32_t>(reinterpret_cast<uintptr_t>(c.lb) >> 8);
+    uint32_t h = tag * 0x9E3779B1u ^ static_cast<uint32_t>(p) * 0x85EBCA77u ^ static_cast<uint32_t>(chain) * 0xC2B2AE3Du ^
+                 site * 0x27D4EB2Fu;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    const int n = (h & 3) == 0 ? static_cast<int>((h >> 8) & 31) : 0;   // a quarter of the tiles, up to ~100 us
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+  } else {
+    (void)c; (void)p; (void)chain; (void)site;
+  }
+}
+
+// The state entering position p in scan order, for the V channels of one lane.  The words of positions
+// p-1, p-2, ... are read in windows of W, walking back past positions that have published only their
+// aggregate (the chunk's affine map) to the nearest one whose inclusive word (the state at the end of its
+// chunk) is out; position 0 publishes its inclusive word without waiting, so the walk always ends.  The
+// carry is then that state advanced through the passed aggregates one at a time, in scan order: exactly
+// the chain of apply(aggregate, state) each tile publishes as its inclusive word, so the result does not
+// depend on how far a walk went (it would if the aggregates were composed with each other first, which
+// rounds differently).  Aggregates of the last window come from registers, earlier ones are re-read
+// (a word never changes once tagged).  All V channels of the lane walk together: one predecessor's words
+// for every channel are loaded in the same round (its publishing lane wrote them together).
 #ifndef PR_LB_W1
 #define PR_LB_W1 2   // look-back window (predecessors per round) for state size 1
 #endif
 template <int S, int V, int TW, int NSLOT, int W>
 DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
-#if PR_LB_JOINT
-  // all V channels of the lane walk together: one predecessor's words for every channel are loaded
-  // in the same round (its publishing lane wrote them together), so V channels cost one walk
-  Aff<S> acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = aff_id<S>();
-  int64_t m = tl.p - 1;
+  int64_t m = tl.p - 1;   // this round's window: positions m, m-1, ..., m-W+1
   bool done = false;
   while (!done) {
     uint64_t wi[W][V][S], wa[W][V][NA];
@@ -398,6 +421,7 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
       }
     }
     bool stalled = false;
+    int passed = 0;   // positions of this window whose aggregate the walk passed
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       if (done || stalled) continue;
@@ -415,81 +439,42 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
           float x[S];
 #pragma unroll
           for (int k = 0; k < S; ++k) x[k] = word_val(wi[j][v][k]);
-          apply(acc[v], x);
+          // positions m-j+1 .. m, in scan order: this window's slots j-1 .. 0
+#pragma unroll
+          for (int jj = W - 1; jj >= 0; --jj) {
+            if (jj < j) {
+              Aff<S> e;
+#pragma unroll
+              for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[jj][v][k]));
+              apply(e, x);
+            }
+          }
+          // positions m+1 .. p-1, passed in earlier rounds
+          for (int64_t pos = m + 1; pos < tl.p; ++pos) {
+            Aff<S> e;
+#pragma unroll
+            for (int k = 0; k < NA; ++k)
+              aff_set(e, k, word_val(ld_word(word_at<S, TW, NSLOT>(c, pos, tl.chain, S + k, tl.qlane * V + v))));
+            apply(e, x);
+          }
 #pragma unroll
           for (int k = 0; k < S; ++k) carry[v][k] = x[k];
         }
+#if PR_LB_STRESS
+        atomicMax(&g_lb_max_depth, static_cast<uint32_t>(tl.p - 1 - (m - j)));
+#endif
         done = true;
       } else if (agg_ok) {
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          Aff<S> e;
-#pragma unroll
-          for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[j][v][k]));
-          acc[v] = compose(acc[v], e);
-        }
-        --m;
+        ++passed;
       } else {
         stalled = true;
       }
     }
-    if (!done && stalled) __builtin_amdgcn_s_sleep(1);
-  }
-#else
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int q = tl.qlane * V + v;
-    Aff<S> acc = aff_id<S>();
-    int64_t m = tl.p - 1;
-    bool done = false;
-    while (!done) {
-      uint64_t wi[W][S], wa[W][NA];
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        const int64_t mm = m - j;
-        if (mm >= 0) {
-#pragma unroll
-          for (int k = 0; k < S; ++k) wi[j][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, k, q));
-#pragma unroll
-          for (int k = 0; k < NA; ++k) wa[j][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, S + k, q));
-        } else {
-#pragma unroll
-          for (int k = 0; k < S; ++k) wi[j][k] = 0;
-#pragma unroll
-          for (int k = 0; k < NA; ++k) wa[j][k] = 0;
-        }
-      }
-      bool stalled = false;
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        if (done || stalled) continue;
-        bool inc_ok = true, agg_ok = true;
-#pragma unroll
-        for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[j][k], c.tag);
-#pragma unroll
-        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[j][k], c.tag);
-        if (inc_ok) {
-          float x[S];
-#pragma unroll
-          for (int k = 0; k < S; ++k) x[k] = word_val(wi[j][k]);
-          apply(acc, x);
-#pragma unroll
-          for (int k = 0; k < S; ++k) carry[v][k] = x[k];
-          done = true;
-        } else if (agg_ok) {
-          Aff<S> e;
-#pragma unroll
-          for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[j][k]));
-          acc = compose(acc, e);
-          --m;
-        } else {
-          stalled = true;
-        }
-      }
-      if (!done && stalled) __builtin_amdgcn_s_sleep(1);
+    if (!done) {
+      m -= passed;
+      if (stalled) __builtin_amdgcn_s_sleep(1);
     }
   }
-#endif
 }
 
 // max(x, x of another lane) over a DPP lane pattern; rows outside ROWS read 0 (keep x)
@@ -676,11 +661,13 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
       Op::init_state(a, tl, carry);
     } else {
       if (tl.active) {
+        stress_pause(c, tl.p, tl.chain, 0);
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
           for (int k = 0; k < NA; ++k)
             st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, S + k, q0 + v), c.tag, aff_get(tagg[v], k));
+        stress_pause(c, tl.p, tl.chain, 1);
         lookback<S, V, TW, NSLOT, Op::LB_WINDOW>(c, tl, carry);
       } else {
 #pragma unroll
@@ -1291,6 +1278,7 @@ struct NewtonOp {
       // publish this tile's last state (the h^k the next tile's first step needs), then take the
       // previous tile's: the trajectory is updated in place, so it cannot be re-read from memory
       if (tl.last_seg && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
+        stress_pause(c, tl.p, tl.chain, 2);
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -1843,6 +1831,7 @@ DEV void fused_leave(const Common& c, int64_t region, const Tile& tl,
   if (tl.last_seg && tl.active && tl.nvalid == L && tl.p + 1 < c.n_chunks) {
     Common cn = c;
     cn.lb += region;
+    stress_pause(cn, tl.p, tl.chain, 3);
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -2517,7 +2506,7 @@ const char* pararnn_status_string(int s) {
     case PARARNN_ERR_UNSUPPORTED: return "unsupported configuration";
     case PARARNN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PARARNN_ERR_HIP: return "HIP runtime error";
-    case PARARNN_ERR_DIVERGED: return "Newton diverged (non-finite residual)";
+    case PARARNN_ERR_DIVERGED: return "Newton diverged (non-finite residual, or the budget ended above the starting residual)";
     default: return "unknown status";
   }
 }
@@ -2664,6 +2653,11 @@ pararnn_status pararnn_newton_report(const pararnn_problem* pb, const pararnn_ne
       if (r < op->tol) { iters = k + 1; conv = 1; break; }
     }
   }
+  // tolerance mode, the budget spent without convergence: a last residual above the one of the iterate
+  // Newton started from (after the Picard sweeps) is divergence too
+  const int k0 = op->picard_iters;
+  if (op->tol > 0.0f && out == PARARNN_OK && !conv && iters - 1 > k0 && report->residual[iters - 1] > report->residual[k0])
+    out = PARARNN_ERR_DIVERGED;
   for (int k = iters; k < K; ++k) report->residual[k] = 0.0f;
   report->iters = iters;
   report->converged = conv;
@@ -2756,5 +2750,19 @@ pararnn_status pararnn_scan_vjp(const pararnn_problem* pb, const float* s, const
   if (!ws || !aligned(ws, 256) || ws_bytes < ve.ws(pb)) return PARARNN_ERR_WORKSPACE;
   return ve.run(pb, s, g, d_pre, d_w, d_bias, d_s0, lambda_out, ws, static_cast<hipStream_t>(stream));
 }
+
+#if PR_LB_STRESS
+// (libraries built with -DPR_LB_STRESS=1 only; declared in pararnn_debug.h)
+int pararnn_debug_lookback_depth(int reset) {
+  uint32_t d = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return PARARNN_ERR_HIP;
+  if (hipMemcpyFromSymbol(&d, HIP_SYMBOL(pr::g_lb_max_depth), sizeof d) != hipSuccess) return PARARNN_ERR_HIP;
+  if (reset) {
+    const uint32_t z = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(pr::g_lb_max_depth), &z, sizeof z) != hipSuccess) return PARARNN_ERR_HIP;
+  }
+  return static_cast<int>(d);
+}
+#endif
 
 }  // extern "C"

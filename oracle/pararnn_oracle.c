@@ -587,7 +587,7 @@ int or_newton(const or_problem* p, const float* init_guess, int init_mode, int p
  * S = 1: a is [B][T][D], b is [B][T][D].
  * S = 2: a is [4][B][T][D] (A00, A01, A10, A11 row-major), b is [2][B][T][D].
  * This is the recurrence that every Newton linear solve reduces to
- * (pararnn-torch README, "Method": each linear solve is an associative scan);
+ * (pararnn-torch README, "Method": the linearised system is solved by a scan along time);
  * here it is evaluated by its definition, one step after another.
  */
 

@@ -56,5 +56,16 @@ def sample_channels(B, D, n, seed):
     return sorted(idx)
 
 
+def lane_channels(B, D, n_extra, seed):
+    """Sampled channels that hold every lane position of a tile: 64 consecutive channels of one batch row,
+    starting at a multiple of 64 (the kernels' tiles are 32 or 64 channels wide and start at multiples of
+    their width), plus the edges and n_extra random channels."""
+    rng = np.random.default_rng(seed)
+    b0 = int(rng.integers(B))
+    d0 = 64 * int(rng.integers(max(1, D // 64)))
+    idx = {(b0, d) for d in range(d0, min(d0 + 64, D))}
+    return sorted(idx | set(sample_channels(B, D, n_extra, seed)))
+
+
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0

@@ -13,6 +13,7 @@ from nonlinear_rnn_solve_amd import api, build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pararnn.h")
+DEBUG_HEADER = os.path.join(ROOT, "include", "pararnn_debug.h")
 
 
 @pytest.fixture(scope="module")
@@ -22,8 +23,8 @@ def lib():
     return api.load_library()
 
 
-def declared_functions():
-    txt = open(HEADER).read()
+def declared_functions(header=HEADER):
+    txt = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:size_t|pararnn_status|const char\*|int)\s+(pararnn_\w+)\s*\(", txt, re.M)))
 
 
@@ -35,6 +36,19 @@ def test_library_exports_every_declared_function(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (pararnn_\w+)", out))
     assert exported == set(names)
+
+
+def test_stress_build_exports_the_same_and_its_debug_query(lib):
+    # the look-back stress build: the same entry points plus the one pararnn_debug.h declares
+    if not os.path.exists(api.STRESS_LIB_PATH):
+        build.build(verbose=False)
+    debug = declared_functions(DEBUG_HEADER)
+    assert debug == ["pararnn_debug_lookback_depth"]
+    out = subprocess.run(["nm", "-D", "--defined-only", api.STRESS_LIB_PATH], capture_output=True, text=True).stdout
+    assert set(re.findall(r"\bT (pararnn_\w+)", out)) == set(declared_functions()) | set(debug)
+    with api.using_library(api.STRESS_LIB_PATH) as slib:
+        assert slib.pararnn_abi_version() == api.ABI_VERSION
+    assert api.library_path() != api.STRESS_LIB_PATH
 
 
 def test_struct_layouts_match_header(tmp_path):

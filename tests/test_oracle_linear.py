@@ -1,8 +1,8 @@
 """Pins for the oracle's linear recurrence (forward / reverse, state size 1 and 2).
 
 The linear recurrence s_t = A_t s_{t-1} + b_t is what every Newton linear solve
-reduces to (pararnn-torch README, "Method": each linear solve is an associative
-scan over time).  The oracle evaluates it step by step; these tests check it
+reduces to (pararnn-torch README, "Method": the linearised system is solved by a
+parallel scan along time).  The oracle evaluates it step by step; these tests check it
 against closed forms and brute-force sums that share nothing with it.
 """
 import numpy as np
