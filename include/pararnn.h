@@ -196,6 +196,23 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* prob, const pararnn_n
                                     float* s_out, void* ws, size_t ws_bytes, void* stream,
                                     pararnn_report* report);
 
+/* pararnn_newton_solve_noalloc -- pararnn_newton_solve without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is a static device array of PARARNN_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends; the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).  The first call on each device looks up that device's address of the
+ * array (hipGetSymbolAddress, with the device current): make it outside graph capture.
+ *   Same arguments, results, report and errors as pararnn_newton_solve, bit for bit.  With
+ * opts->fuse_iters = 0 the launch length is the library's, shortened until the look-back words fit the
+ * array; a problem whose workspace does not fit even at one launch per iteration (or at an explicit
+ * fuse_iters) returns PARARNN_ERR_WORKSPACE before launching anything.
+ *   All calls on one GPU share its array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made.  Each call clears the parts that must start at zero with a kernel,
+ * so the previous call's contents do not matter. */
+#define PARARNN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+pararnn_status pararnn_newton_solve_noalloc(const pararnn_problem* prob, const pararnn_newton_opts* opts,
+                                            float* s_out, void* stream, pararnn_report* report);
+
 /* The same solve in three steps, for callers that time, checkpoint or interleave work between
  * iterations.  pararnn_newton_solve(...) with fuse_iters = 1 is exactly: prepare; iterate k = 0 ..
  * max_iters-1; [final residual]; report (with fused launches it returns the same bits).  All share

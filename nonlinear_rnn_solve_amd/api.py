@@ -115,6 +115,8 @@ def load_library():
     lib.pararnn_newton_workspace_bytes.argtypes = [vp, vp]
     lib.pararnn_newton_solve.restype = i32
     lib.pararnn_newton_solve.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    lib.pararnn_newton_solve_noalloc.restype = i32
+    lib.pararnn_newton_solve_noalloc.argtypes = [vp, vp, vp, vp, vp]
     lib.pararnn_newton_prepare.restype = i32
     lib.pararnn_newton_prepare.argtypes = [vp, vp, vp, sz, vp]
     lib.pararnn_newton_iterate.restype = i32
@@ -281,7 +283,7 @@ def _on_device(pos, name):
 @_on_device(1, "pre")
 def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, init_guess=None, out=None,
                  final_residual=False, report=True, on_iteration=None, warm_start=False, cu_seqlens=None,
-                 picard_iters=0, fuse_iters=0):
+                 picard_iters=0, fuse_iters=0, noalloc=False):
     """Newton solve of F(H) = 0.  Returns (trajectory [S, B, T, D] float32, NewtonReport or None).
 
     pre: G planes [B, T, D] (float32 or bfloat16) on the GPU; w, bias: [G, D] float32 (head_gru: w is
@@ -299,6 +301,8 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     on_iteration: optional callable(k, phase) with phase "before"/"after", invoked on the host around the
     launch of iteration k (e.g. to record stream events); the solve then runs through the step-wise
     entry points prepare / iterate / report, which launch exactly the same kernels.
+    noalloc: call pararnn_newton_solve_noalloc, whose workspace is the library's static device array (no
+    workspace is allocated here either); calls that overlap on one GPU must not use it.
     """
     lib = load_library()
     st, c, G, S, (B, T, D) = _problem(cell, pre, w, bias, s0, cu_seqlens)
@@ -315,10 +319,16 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
     opts = _Opts(int(max_iters or 0), float(tol), init_guess.data_ptr() if init_guess is not None else None,
                  1 if final_residual else 0, INIT_WARM if warm_start else INIT_ZERO, int(picard_iters),
                  int(fuse_iters))
-    nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
-    ws = _workspace(nbytes, dev, "newton")
     rep = _Report() if report else None
     stream = _stream(dev)
+    if noalloc:
+        if on_iteration is not None:
+            raise ValueError("on_iteration needs the step-wise entry points, which take a workspace")
+        rc = lib.pararnn_newton_solve_noalloc(ctypes.byref(st), ctypes.byref(opts), _ptr(out), stream,
+                                              ctypes.byref(rep) if rep is not None else None)
+        return _newton_result(rc, rep, final_residual, out)
+    nbytes = lib.pararnn_newton_workspace_bytes(ctypes.byref(st), ctypes.byref(opts))
+    ws = _workspace(nbytes, dev, "newton")
     if on_iteration is None:
         rc = lib.pararnn_newton_solve(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
                                       stream, ctypes.byref(rep) if rep is not None else None)
@@ -335,6 +345,10 @@ def newton_solve(cell, pre, w=None, bias=None, max_iters=3, tol=0.0, s0=None, in
         if rc == 0:
             rc = lib.pararnn_newton_report(ctypes.byref(st), ctypes.byref(opts), _ptr(out), _ptr(ws), ws.numel(),
                                            stream, ctypes.byref(rep) if rep is not None else None)
+    return _newton_result(rc, rep, final_residual, out)
+
+
+def _newton_result(rc, rep, final_residual, out):
     r = None
     if rep is not None:
         res = [float(rep.residual[i]) for i in range(rep.n_residual)]

@@ -38,6 +38,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "pararnn.h"
 #include "pararnn_debug.h"
@@ -2493,6 +2494,34 @@ VjpEntry pick_vjp(const pararnn_problem* pb) {
 }  // namespace
 
 // ================================================================================================
+// the allocation-free solve's workspace: one static device array, PARARNN_NOALLOC_SCRATCH_BYTES long,
+// that every GPU the library runs on holds until the process ends.  Host code never passes the array's
+// name to a kernel (in host code it is a host-side stand-in); it takes each device's own address of it
+// once, with that device current, and uses that address.
+// ================================================================================================
+static __device__ __align__(256) unsigned char scratch[PARARNN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device: the address of its copy of scratch (null until looked up)
+
+pararnn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PARARNN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PARARNN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PARARNN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PARARNN_OK;
+}
+}  // namespace
+
+// ================================================================================================
 // C ABI
 // ================================================================================================
 extern "C" {
@@ -2578,8 +2607,9 @@ int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   return m < 1 ? 1 : m;
 }
 
-pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
-                            bool need_out, void* ws, size_t ws_bytes) {
+// the arguments of a Newton entry point other than its workspace
+pararnn_status newton_check_args(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
+                                 bool need_out) {
   pararnn_status rc = check_problem(pb);
   if (rc) return rc;
   if (!op || op->max_iters < 0 || op->max_iters > PARARNN_MAX_ITERS) return PARARNN_ERR_INVALID_ARG;
@@ -2591,6 +2621,13 @@ pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts
   if (problem_N(pb) == 0) return PARARNN_OK;
   if (need_out && (!s_out || !aligned(s_out, 8))) return PARARNN_ERR_INVALID_ARG;
   if (op->init_guess && !aligned(op->init_guess, 8)) return PARARNN_ERR_INVALID_ARG;
+  return PARARNN_OK;
+}
+
+pararnn_status newton_check(const pararnn_problem* pb, const pararnn_newton_opts* op, const float* s_out,
+                            bool need_out, void* ws, size_t ws_bytes) {
+  pararnn_status rc = newton_check_args(pb, op, s_out, need_out);
+  if (rc || problem_N(pb) == 0) return rc;
   if (!ws || !aligned(ws, 256) || ws_bytes < pick_newton(pb).ws(pb, fuse_len(pb, op))) return PARARNN_ERR_WORKSPACE;
   return PARARNN_OK;
 }
@@ -2700,6 +2737,27 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
   if (rc) return rc;
   if (!report && !op->final_residual) return PARARNN_OK;
   return pararnn_newton_report(pb, op, s_out, ws, ws_bytes, stream, report);
+}
+
+pararnn_status pararnn_newton_solve_noalloc(const pararnn_problem* pb, const pararnn_newton_opts* op, float* s_out,
+                                            void* stream, pararnn_report* report) {
+  pararnn_status rc = newton_check_args(pb, op, s_out, true);
+  if (rc) return rc;
+  if (problem_N(pb) == 0) return pararnn_newton_report(pb, op, s_out, nullptr, 0, stream, report);
+  // the library's launch length, shortened until its look-back words fit the scratch (the result is the
+  // same bit for bit for every launch length); an explicit fuse_iters is taken as given
+  pararnn_newton_opts o = *op;
+  const NewtonEntry ne = pick_newton(pb);
+  if (o.fuse_iters == 0) {
+    int m = fuse_len(pb, &o);
+    while (m > 1 && ne.ws(pb, m) > PARARNN_NOALLOC_SCRATCH_BYTES) --m;
+    o.fuse_iters = m;
+  }
+  if (ne.ws(pb, fuse_len(pb, &o)) > PARARNN_NOALLOC_SCRATCH_BYTES) return PARARNN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return pararnn_newton_solve(pb, &o, s_out, ws, PARARNN_NOALLOC_SCRATCH_BYTES, stream, report);
 }
 
 int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {

@@ -30,7 +30,7 @@ def declared_functions(header=HEADER):
 
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()], capture_output=True, text=True).stdout
@@ -225,3 +225,17 @@ def test_automatic_budget_is_the_measured_kstar(lib):
     assert lib.pararnn_newton_budget(1, 0, -1, 0) == -1
     assert lib.pararnn_newton_budget(1, 0, 100, 65) == -1
     assert api.newton_budget("gru", 4096) == lib.pararnn_newton_budget(1, 0, 4096, 0)
+
+
+def test_noalloc_solve_validates_before_touching_the_gpu(lib):
+    # argument errors and a problem too large for the static array are reported before any HIP call
+    p = _problem(cell=2, dtype=0, B=4, T=8192, D=2048)
+    o = api._Opts(8, 1e-5, None, 0, 0, 0, 8)                  # 8 fused iterations: 320 MiB of words
+    assert lib.pararnn_newton_solve_noalloc(ctypes.byref(p), ctypes.byref(o), ctypes.c_void_p(4096), None,
+                                            None) == -3
+    assert lib.pararnn_newton_solve_noalloc(ctypes.byref(p), ctypes.byref(o), None, None, None) == -1
+    o.max_iters = 65
+    assert lib.pararnn_newton_solve_noalloc(ctypes.byref(p), ctypes.byref(o), ctypes.c_void_p(4096), None,
+                                            None) == -1
+    assert lib.pararnn_newton_solve_noalloc(None, ctypes.byref(o), ctypes.c_void_p(4096), None, None) == -1
+
