@@ -2213,13 +2213,23 @@ bool grid_ok(const Geo& g) {
 // ---------------- validation ----------------
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// nonnegative B, T, D (B and D at most 2^40) whose element count, times the 4 planes of the largest cell and
+// 4 bytes an element, fits int64 (every product is tested by division before it is formed)
+bool sizes_fit(int64_t B, int64_t T, int64_t D) {
+  if (B < 0 || T < 0 || D < 0) return false;
+  if (B > (int64_t(1) << 40) || D > (int64_t(1) << 40)) return false;
+  if (B == 0 || T == 0 || D == 0) return true;
+  const int64_t lim = INT64_MAX / 16;
+  if (B > lim / D) return false;
+  return T <= lim / (B * D);
+}
+
 pararnn_status check_problem(const pararnn_problem* pb) {
   if (!pb) return PARARNN_ERR_INVALID_ARG;
   if (pb->cell < CELL_LINEAR || pb->cell > CELL_HEAD_GRU) return PARARNN_ERR_INVALID_ARG;
   if (pb->pre_dtype != PARARNN_F32 && pb->pre_dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
   if (pb->B < 0 || pb->T < 0 || pb->D < 0) return PARARNN_ERR_INVALID_ARG;
-  if (pb->B > (int64_t(1) << 40) || pb->D > (int64_t(1) << 40)) return PARARNN_ERR_INVALID_ARG;
-  if (pb->B > 0 && pb->D > 0 && pb->T > INT64_MAX / (pb->B * pb->D) / 4) return PARARNN_ERR_INVALID_ARG;
+  if (!sizes_fit(pb->B, pb->T, pb->D)) return PARARNN_ERR_INVALID_ARG;
   if (pb->cell == CELL_HEAD_GRU) {
     if (pb->head_size < 1 || (pb->D > 0 && pb->D % pb->head_size != 0)) return PARARNN_ERR_INVALID_ARG;
     if (pb->head_size != 16 && pb->head_size != 32 && pb->head_size != 64) return PARARNN_ERR_UNSUPPORTED;
@@ -2770,7 +2780,7 @@ int pararnn_newton_budget(int cell, int init_mode, int64_t T, int max_iters) {
 }
 
 size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {
-  if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return 0;
+  if ((S != 1 && S != 2) || !sizes_fit(B, T, D)) return 0;
   if (B * T * D == 0) return kHeader;
   return pick_scan(S, PARARNN_F32, 0, false).ws(B, T, D);
 }
@@ -2778,9 +2788,8 @@ size_t pararnn_scan_workspace_bytes(int S, int64_t B, int64_t T, int64_t D) {
 pararnn_status pararnn_linear_scan(int S, int64_t B, int64_t T, int64_t D, int dtype, const void* a, const void* b,
                                    const float* s0, const int32_t* cu_seqlens, int64_t n_seqs, float* s_out,
                                    int reverse, void* ws, size_t ws_bytes, void* stream) {
-  if ((S != 1 && S != 2) || B < 0 || T < 0 || D < 0) return PARARNN_ERR_INVALID_ARG;
+  if ((S != 1 && S != 2) || !sizes_fit(B, T, D)) return PARARNN_ERR_INVALID_ARG;
   if (dtype != PARARNN_F32 && dtype != PARARNN_BF16) return PARARNN_ERR_INVALID_ARG;
-  if (B > 0 && D > 0 && T > INT64_MAX / (B * D) / 4) return PARARNN_ERR_INVALID_ARG;
   if (B * T * D == 0) return PARARNN_OK;
   if (!a || !b || !s_out) return PARARNN_ERR_INVALID_ARG;
   if (!aligned(a, 4) || !aligned(b, 4) || !aligned(s_out, 4) || (s0 && !aligned(s0, 4))) return PARARNN_ERR_INVALID_ARG;
