@@ -1513,15 +1513,37 @@ struct VjpOp {
     // loads first: evaluation e (0..L) is the cell step at t = t_lo + e, which needs U_t and
     // s_{t-1}; e = L belongs to the next lane's first step and only contributes its Jacobian
     float u[G][L + 1][V], sp[S][L + 1][V], gv[L][V];
+    if (!MASKED && a.c.off32) {
+      // full lanes: every address is the wave's uniform base element plus a step offset (scalar) and the
+      // lane's 32-bit offset, so no load needs 64-bit vector address arithmetic; the state before the very
+      // first step is s0 (below), not loaded
 #pragma unroll
-    for (int e = 0; e <= L; ++e) {
-      const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
-      const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+      for (int e = 0; e <= L; ++e) {
+        const int64_t ub = tl.wbase + e * D;
 #pragma unroll
-      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
+        for (int g = 0; g < G; ++g) ldv_u<V, DT>(a.pre[g], ub, tl.loff, u[g][e]);
 #pragma unroll
-      for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
-      if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
+        for (int k = 0; k < S; ++k) {
+          if (e > 0 || tl.t_lo != 0) {
+            ldv_u<V, DT_F32>(a.s + k * N, ub - D, tl.loff, sp[k][e]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) sp[k][e][v] = 0.0f;
+          }
+        }
+        if (e < L) ldv_u<V, DT_F32>(a.g, ub, tl.loff, gv[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e <= L; ++e) {
+        const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
+        const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
+#pragma unroll
+        for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
+        if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
+      }
     }
     if (tl.t_lo == 0) {
       float x[V][S];
@@ -1627,6 +1649,7 @@ struct VjpOp {
       for (int j = 0; j < NP; ++j) par[v][j] = 0.0f;
     if (tl.active) {
       const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
+      const bool fast = a.c.off32 && tl.nvalid == L;   // every step of the lane exists
 #pragma unroll
       for (int s = 0; s < L; ++s) {
         const int i = L - 1 - s;
@@ -1688,8 +1711,13 @@ struct VjpOp {
           }
         }
         const int64_t idx = base + i * D;
+        if (fast) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
+          for (int g = 0; g < G; ++g) stv_u<V>(a.d_pre + g * N, tl.wbase + i * D, tl.loff, du[g]);
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
+        }
         if (a.lambda_out) {
 #pragma unroll
           for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);
@@ -2559,18 +2587,30 @@ namespace {
 // oracle -- K*(T) as the pararnn-torch README defines it ("Method") and measures it in its
 // long-context campaign ("Benchmarks").  A
 // length between grid points takes the next larger point's budget; beyond the grid, one more.
-struct KStarRow { int32_t cell, init; int64_t T; int32_t k; };
+// With each entry, the iteration count tolerance mode reached on the same inputs (the first k with R_k < tol,
+// plus one) at tol = 1e-4, 1e-5 and 1e-6: the length of the speculative fused launch (fuse_len).
+struct KStarRow { int32_t cell, init; int64_t T; int32_t k; int32_t stop[3]; };
 constexpr KStarRow kKStar[] = {
-    {CELL_GRU, PARARNN_INIT_ZERO, 1024, 3}, {CELL_GRU, PARARNN_INIT_WARM, 1024, 3},
-    {CELL_GRU, PARARNN_INIT_ZERO, 4096, 3}, {CELL_GRU, PARARNN_INIT_WARM, 4096, 3},
-    {CELL_GRU, PARARNN_INIT_ZERO, 16384, 3}, {CELL_GRU, PARARNN_INIT_WARM, 16384, 3},
-    {CELL_GRU, PARARNN_INIT_ZERO, 65536, 3}, {CELL_GRU, PARARNN_INIT_WARM, 65536, 3},
-    {CELL_GRU, PARARNN_INIT_ZERO, 131072, 3}, {CELL_GRU, PARARNN_INIT_WARM, 131072, 3},
-    {CELL_LSTM, PARARNN_INIT_ZERO, 1024, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 1024, 4},
-    {CELL_LSTM, PARARNN_INIT_ZERO, 4096, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 4096, 4},
-    {CELL_LSTM, PARARNN_INIT_ZERO, 16384, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 16384, 4},
-    {CELL_LSTM, PARARNN_INIT_ZERO, 65536, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 65536, 4},
-    {CELL_LSTM, PARARNN_INIT_ZERO, 131072, 4}, {CELL_LSTM, PARARNN_INIT_WARM, 131072, 4},
+    {CELL_GRU, PARARNN_INIT_ZERO, 1024, 3, {4, 5, 5}},
+    {CELL_GRU, PARARNN_INIT_WARM, 1024, 3, {4, 4, 5}},
+    {CELL_GRU, PARARNN_INIT_ZERO, 4096, 3, {4, 5, 5}},
+    {CELL_GRU, PARARNN_INIT_WARM, 4096, 3, {4, 4, 5}},
+    {CELL_GRU, PARARNN_INIT_ZERO, 16384, 3, {4, 5, 5}},
+    {CELL_GRU, PARARNN_INIT_WARM, 16384, 3, {4, 4, 4}},
+    {CELL_GRU, PARARNN_INIT_ZERO, 65536, 3, {4, 5, 5}},
+    {CELL_GRU, PARARNN_INIT_WARM, 65536, 3, {4, 4, 5}},
+    {CELL_GRU, PARARNN_INIT_ZERO, 131072, 3, {4, 5, 5}},
+    {CELL_GRU, PARARNN_INIT_WARM, 131072, 3, {4, 4, 5}},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 1024, 4, {5, 5, 5}},
+    {CELL_LSTM, PARARNN_INIT_WARM, 1024, 4, {5, 5, 5}},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 4096, 4, {5, 5, 5}},
+    {CELL_LSTM, PARARNN_INIT_WARM, 4096, 4, {5, 5, 5}},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 16384, 4, {5, 5, 6}},
+    {CELL_LSTM, PARARNN_INIT_WARM, 16384, 4, {5, 5, 5}},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 65536, 4, {5, 6, 6}},
+    {CELL_LSTM, PARARNN_INIT_WARM, 65536, 4, {5, 5, 6}},
+    {CELL_LSTM, PARARNN_INIT_ZERO, 131072, 4, {5, 5, 6}},
+    {CELL_LSTM, PARARNN_INIT_WARM, 131072, 4, {5, 5, 5}},
 };
 
 int auto_iters(int cell, int init, int64_t T) {
@@ -2580,6 +2620,20 @@ int auto_iters(int cell, int init, int64_t T) {
     if (r.cell != cell || r.init != init) continue;
     if (T <= r.T) return r.k;
     last = r.k;
+  }
+  return last + 1;
+}
+
+// the tolerance-mode iteration count measured with K*(T), at the smallest of the table's tolerances (1e-4,
+// 1e-5, 1e-6) at or above tol (a count no larger than tol's own on those inputs); beyond the grid, one more
+int stop_iters(int cell, int init, int64_t T, float tol) {
+  if (cell == CELL_LINEAR) return 1;
+  const int col = tol > 1e-5f ? 0 : (tol > 1e-6f ? 1 : 2);
+  int last = 0;
+  for (const KStarRow& r : kKStar) {
+    if (r.cell != cell || r.init != init) continue;
+    if (T <= r.T) return r.stop[col];
+    last = r.stop[col];
   }
   return last + 1;
 }
@@ -2597,13 +2651,13 @@ constexpr float kKStarTau = 1e-4f;
 // Iterations per launch of a solve's fused passes (1: one launch per iteration).  Fixed budget: all
 // K iterations, PARARNN_MAX_FUSE at a time.  Tolerance mode: the first pass runs speculatively (a
 // re-run corrects it when the stop came earlier; single launches follow when it came later) for the
-// measured K*(T) iterations, and one more when tol is at or below the table's agreement bar: the
-// residual R_k of an iterate that misses the unroll by 1e-4 or more is itself no smaller, so the stop
-// rule reads R_{K*} at the earliest, in iteration K* + 1 (the fp64 oracle on the table's inputs stops
-// at K* + 1 or K* + 2 for every cell, first iterate and length of the table at tol 1e-4 .. 1e-6).
-// opts->fuse_iters overrides the length; Picard sweeps and the cells without a fused kernel run one
-// launch per iteration.  NULL opts: the longest pass any options can ask for (the workspace size that
-// fits every solve of the problem).
+// iteration count tolerance mode reached on the K*(T) campaign's inputs at the nearest of its
+// tolerances at or above tol (stop_iters: K*(T) + 1 or K*(T) + 2 on every cell, first iterate and length
+// of the grid), or K*(T) when tol is looser than the table's 1e-4 agreement bar.  Speculating short costs
+// a single launch per missing iteration, speculating long a re-run of the pass, so the bracket's looser
+// end is taken.  opts->fuse_iters overrides the length; Picard sweeps and the cells without a fused
+// kernel run one launch per iteration.  NULL opts: the longest pass any options can ask for (the
+// workspace size that fits every solve of the problem).
 int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   if (!pick_newton(pb).fused) return 1;
   if (!op) return PARARNN_MAX_FUSE;
@@ -2611,8 +2665,10 @@ int fuse_len(const pararnn_problem* pb, const pararnn_newton_opts* op) {
   const int K = budget(pb, op);
   int m = PARARNN_MAX_FUSE;
   if (op->fuse_iters > 1) m = op->fuse_iters;
-  else if (op->tol > 0.0f)
-    m = auto_iters(pb->cell, op->init_guess ? PARARNN_INIT_ZERO : op->init_mode, pb->T) + (op->tol <= kKStarTau ? 1 : 0);
+  else if (op->tol > 0.0f) {
+    const int init = op->init_guess ? PARARNN_INIT_ZERO : op->init_mode;
+    m = op->tol <= kKStarTau ? stop_iters(pb->cell, init, pb->T, op->tol) : auto_iters(pb->cell, init, pb->T);
+  }
   m = std::min(m, std::min(K, PARARNN_MAX_FUSE));
   return m < 1 ? 1 : m;
 }

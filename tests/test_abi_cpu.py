@@ -119,12 +119,15 @@ def test_workspace_grows_with_fused_iterations(lib):
     assert one < three < eight == size(None)
     assert (three - one) * 7 == (eight - one) * 2          # the same region size per fused iteration
     assert size(api._Opts(8, 0.0, None, 0, 0, 0, 4)) == size(api._Opts(4, 0.0, None, 0, 0, 0, 0))
-    # tolerance mode: the first launch runs the measured K*(T) (3 for the GRU at this length), one more when
-    # tol is at or below the 1e-4 bar K*(T) was measured at
+    # tolerance mode: the first launch runs the measured K*(T) (3 for the GRU at this length) above the 1e-4
+    # bar K*(T) was measured at, else the count tolerance mode reached on the campaign's inputs (4 at 1e-4,
+    # 5 at 1e-5 here)
     four = size(api._Opts(4, 0.0, None, 0, 0, 0, 0))
+    five = size(api._Opts(5, 0.0, None, 0, 0, 0, 0))
     assert (four - one) * 2 == (three - one) * 3
     assert size(api._Opts(8, 1e-3, None, 0, 0, 0, 0)) == three
-    assert size(api._Opts(8, 1e-4, None, 0, 0, 0, 0)) == size(api._Opts(8, 1e-5, None, 0, 0, 0, 0)) == four
+    assert size(api._Opts(8, 1e-4, None, 0, 0, 0, 0)) == four
+    assert size(api._Opts(8, 1e-5, None, 0, 0, 0, 0)) == five
     assert size(api._Opts(3, 1e-5, None, 0, 0, 0, 0)) == three        # never beyond the budget
     # Picard sweeps, and cells without a fused kernel, use one launch per iteration
     assert size(api._Opts(3, 0.0, None, 0, 0, 1, 0)) == one
@@ -238,4 +241,24 @@ def test_noalloc_solve_validates_before_touching_the_gpu(lib):
     assert lib.pararnn_newton_solve_noalloc(ctypes.byref(p), ctypes.byref(o), ctypes.c_void_p(4096), None,
                                             None) == -1
     assert lib.pararnn_newton_solve_noalloc(None, ctypes.byref(o), ctypes.c_void_p(4096), None, None) == -1
+
+
+def test_speculation_length_is_the_measured_tolerance_mode_count(lib):
+    # in tolerance mode the library's launch length (seen through the workspace size, which grows by one set
+    # of look-back words per fused iteration) is the iteration count the K*(T) campaign's oracle run reached
+    # at the nearest of its tolerances at or above tol (tests/golden/kstar.json), K*(T) above 1e-4
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kstar.json")) as f:
+        gold = json.load(f)
+    cells = {"gru": 1, "lstm": 2}
+    for e in gold["entries"]:
+        p = _problem(cell=cells[e["cell"]], dtype=1 if e["dtype"] == "bf16" else 0, B=gold["B"], T=e["T"], D=gold["D"])
+        init = 1 if e["init"] == "warm" else 0
+        for tol, key in ((1e-4, "0.0001"), (3e-5, "0.0001"), (1e-5, "1e-05"), (2e-6, "1e-05"), (1e-6, "1e-06"),
+                         (1e-9, "1e-06"), (1e-3, None)):
+            want = e["kstar"] if key is None else e["stop_iters"][key]
+            assert e["kstar"] <= want <= e["kstar"] + 2
+            o = api._Opts(8, tol, None, 0, init, 0, 0)
+            m = api._Opts(8, tol, None, 0, init, 0, want)
+            assert lib.pararnn_newton_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == \
+                lib.pararnn_newton_workspace_bytes(ctypes.byref(p), ctypes.byref(m)), (e["cell"], e["init"], e["T"], tol)
 

@@ -216,6 +216,8 @@ def test_stop_rule_below_the_kstar_bar_runs_past_kstar():
         inp = synth.make_inputs(e["cell"], gold["B"], e["T"], gold["D"], dtype=e["dtype"], seed=e["seed"])
         prob = oracle.Problem(e["cell"], inp.pre, inp.w, inp.bias,
                               dtype=oracle.BF16 if e["dtype"] == "bf16" else oracle.F32)
-        for tol in (1e-4, 1e-5):
+        for tol in (1e-4, 1e-5, 1e-6):
             _, res, iters, conv, _ = oracle.newton(prob, 8, tol=tol, warm=e["init"] == "warm")
             assert conv and e["kstar"] + 1 <= iters <= e["kstar"] + 2, (e["cell"], e["init"], e["T"], tol, list(res))
+            # and the golden file's tolerance-mode counts (the speculation table) are these
+            assert iters == e["stop_iters"]["%g" % tol]
