@@ -2,8 +2,9 @@
  * pararnn_debug.h -- entry points of the look-back stress build of libpararnn (the same source compiled
  * with -DPR_LB_STRESS=1 into libpararnn_stress.so).  That build pauses the tiles that publish look-back
  * words (the decoupled look-back that joins time chunks in every scan; pararnn-torch README, "Method":
- * each linear solve is a parallel scan along time) for pseudo-random times, so that later tiles walk far
- * back; its results must equal the plain library's bit for bit.  The plain library does not export this.
+ * the linearised system is solved by a parallel scan along time) for pseudo-random times, so that tiles
+ * take their carry by either path; its results must equal the plain library's bit for bit.  The plain
+ * library does not export this.
  */
 #ifndef PARARNN_DEBUG_H
 #define PARARNN_DEBUG_H
@@ -12,10 +13,10 @@
 extern "C" {
 #endif
 
-/* The deepest look-back walk since the last reset, counted in aggregate words passed before an
- * inclusive word was found (0: every tile found its predecessor's state at once).  Waits for the
- * device; reset != 0 clears the counter after reading it.  Returns the depth (>= 0) or
- * PARARNN_ERR_HIP (-4) when a HIP call fails. */
+/* The deepest look-back walk since the last reset: 0 when every tile took its carry from its predecessor's
+ * inclusive word, 1 once some tile took it from its predecessor's aggregate applied to the inclusive word
+ * before that (the walk never goes deeper).  Waits for the device; reset != 0 clears the counter after
+ * reading it.  Returns the depth (>= 0) or PARARNN_ERR_HIP (-4) when a HIP call fails. */
 int pararnn_debug_lookback_depth(int reset);
 
 #ifdef __cplusplus

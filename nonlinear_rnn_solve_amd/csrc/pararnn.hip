@@ -12,9 +12,13 @@
 //    TW = 64*V consecutive channels (lane = V channels, loads of 4..16 bytes
 //    per lane, a wave reads one contiguous row) by CT = NW*L time steps (wave
 //    w owns steps [w*L, (w+1)*L) of the chunk, each lane walks its L steps
-//    serially in registers).  No MFMA: nothing here is a dense contraction;
-//    the work is bound by HBM bandwidth.
-//  * One kernel per scan / Newton iteration / VJP.  Each tile (1) produces its
+//    serially in registers).  The diagonal cells use no MFMA (no step is a
+//    dense contraction): a kernel that runs one iteration per launch is bound
+//    by HBM bandwidth, the fused pass that runs several (k_fused) by vector
+//    ALU issue.  The head-wise block GRU (head_gru_dev.inc) composes its dense
+//    Jacobian blocks on MFMA.
+//  * One kernel per scan / Newton iteration / VJP (the fused pass: several
+//    iterations per launch, trajectory kept on chip).  Each tile (1) produces its
 //    affine scan elements in registers (loaded, or computed from the cell's
 //    residual and Jacobian), (2) reduces them per lane and across waves
 //    through LDS, (3) obtains the state entering its chunk by a decoupled
@@ -364,7 +368,7 @@ DEV uint64_t* word_at(const Common& c, int64_t p, int chain, int slot, int q) {
 #define PR_LB_STRESS 0
 #endif
 #if PR_LB_STRESS
-__device__ uint32_t g_lb_max_depth;   // deepest walk seen: aggregates applied before an inclusive word
+__device__ uint32_t g_lb_max_depth;   // deepest walk seen: aggregates applied to an inclusive word (0 or 1)
 #endif
 DEV void stress_pause(const Common& c, int64_t p, int chain, uint32_t site) {
   if constexpr (PR_LB_STRESS) {
@@ -382,100 +386,93 @@ DEV void stress_pause(const Common& c, int64_t p, int chain, uint32_t site) {
   }
 }
 
-// The state entering position p in scan order, for the V channels of one lane.  The words of positions
-// p-1, p-2, ... are read in windows of W, walking back past positions that have published only their
-// aggregate (the chunk's affine map) to the nearest one whose inclusive word (the state at the end of its
-// chunk) is out; position 0 publishes its inclusive word without waiting, so the walk always ends.  The
-// carry is then that state advanced through the passed aggregates one at a time, in scan order: exactly
-// the chain of apply(aggregate, state) each tile publishes as its inclusive word, so the result does not
-// depend on how far a walk went (it would if the aggregates were composed with each other first, which
-// rounds differently).  Aggregates of the last window come from registers, earlier ones are re-read
-// (a word never changes once tagged).  All V channels of the lane walk together: one predecessor's words
-// for every channel are loaded in the same round (its publishing lane wrote them together).
-#ifndef PR_LB_W1
-#define PR_LB_W1 2   // look-back window (predecessors per round) for state size 1
-#endif
-template <int S, int V, int TW, int NSLOT, int W>
+// The state entering position p in scan order, for the V channels of one lane: the inclusive word of
+// position p-1 (the state at the end of its chunk), or, once p-1 has published only its aggregate (the
+// chunk's affine map), that map applied to the inclusive word of p-2 -- whichever appears first.  Both are
+// the same bits: p-1 publishes its inclusive word as its aggregate applied to its own carry, which by the
+// same rule is p-2's inclusive word.  So every carry is the sequential chain apply(aggregate, state), and no
+// result depends on timing (a walk that composed several aggregates first would round differently).  The
+// walk never goes deeper than one aggregate; forward progress holds because p-1 and p-2 have smaller
+// tickets (running or done), and position 0 publishes its inclusive word without waiting.  All V channels
+// of the lane wait together: their words were written together by one lane of the predecessor.
+template <int S, int V, int TW, int NSLOT>
 DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
-  int64_t m = tl.p - 1;   // this round's window: positions m, m-1, ..., m-W+1
-  bool done = false;
-  while (!done) {
-    uint64_t wi[W][V][S], wa[W][V][NA];
+  const int64_t p1 = tl.p - 1, p2 = tl.p - 2;
+  bool have_agg = false;   // p-1's aggregate is out (then agg holds it)
+  Aff<S> agg[V];
+#if PR_LB_STRESS
+  uint32_t depth = 0;
+#endif
+  while (true) {
+    uint64_t wi[V][S];
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const int64_t mm = m - j;
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int q = tl.qlane * V + v;
-        if (mm >= 0) {
+      for (int k = 0; k < S; ++k) wi[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, k, tl.qlane * V + v));
+    bool inc_ok = true;
 #pragma unroll
-          for (int k = 0; k < S; ++k) wi[j][v][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, k, q));
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int k = 0; k < NA; ++k) wa[j][v][k] = ld_word(word_at<S, TW, NSLOT>(c, mm, tl.chain, S + k, q));
-        } else {
+      for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[v][k], c.tag);
+    if (inc_ok) {
 #pragma unroll
-          for (int k = 0; k < S; ++k) wi[j][v][k] = 0;
+      for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int k = 0; k < NA; ++k) wa[j][v][k] = 0;
-        }
+        for (int k = 0; k < S; ++k) carry[v][k] = word_val(wi[v][k]);
+      break;
+    }
+    if (!have_agg && p2 >= 0) {
+      uint64_t wa[V][NA];
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < NA; ++k) wa[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, S + k, tl.qlane * V + v));
+      bool agg_ok = true;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[v][k], c.tag);
+      if (agg_ok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < NA; ++k) aff_set(agg[v], k, word_val(wa[v][k]));
+        have_agg = true;
       }
     }
-    bool stalled = false;
-    int passed = 0;   // positions of this window whose aggregate the walk passed
+    if (have_agg) {
+      uint64_t w2[V][S];
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      if (done || stalled) continue;
-      bool inc_ok = true, agg_ok = true;
+      for (int v = 0; v < V; ++v)
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
+        for (int k = 0; k < S; ++k) w2[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p2, tl.chain, k, tl.qlane * V + v));
+      bool ok2 = true;
 #pragma unroll
-        for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[j][v][k], c.tag);
+      for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[j][v][k], c.tag);
-      }
-      if (inc_ok) {
+        for (int k = 0; k < S; ++k) ok2 = ok2 && word_ok(w2[v][k], c.tag);
+      if (ok2) {
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           float x[S];
 #pragma unroll
-          for (int k = 0; k < S; ++k) x[k] = word_val(wi[j][v][k]);
-          // positions m-j+1 .. m, in scan order: this window's slots j-1 .. 0
-#pragma unroll
-          for (int jj = W - 1; jj >= 0; --jj) {
-            if (jj < j) {
-              Aff<S> e;
-#pragma unroll
-              for (int k = 0; k < NA; ++k) aff_set(e, k, word_val(wa[jj][v][k]));
-              apply(e, x);
-            }
-          }
-          // positions m+1 .. p-1, passed in earlier rounds
-          for (int64_t pos = m + 1; pos < tl.p; ++pos) {
-            Aff<S> e;
-#pragma unroll
-            for (int k = 0; k < NA; ++k)
-              aff_set(e, k, word_val(ld_word(word_at<S, TW, NSLOT>(c, pos, tl.chain, S + k, tl.qlane * V + v))));
-            apply(e, x);
-          }
+          for (int k = 0; k < S; ++k) x[k] = word_val(w2[v][k]);
+          apply(agg[v], x);
 #pragma unroll
           for (int k = 0; k < S; ++k) carry[v][k] = x[k];
         }
 #if PR_LB_STRESS
-        atomicMax(&g_lb_max_depth, static_cast<uint32_t>(tl.p - 1 - (m - j)));
+        depth = 1;
 #endif
-        done = true;
-      } else if (agg_ok) {
-        ++passed;
-      } else {
-        stalled = true;
+        break;
       }
     }
-    if (!done) {
-      m -= passed;
-      if (stalled) __builtin_amdgcn_s_sleep(1);
-    }
+    __builtin_amdgcn_s_sleep(1);
   }
+#if PR_LB_STRESS
+  atomicMax(&g_lb_max_depth, depth);
+#endif
 }
 
 // max(x, x of another lane) over a DPP lane pattern; rows outside ROWS read 0 (keep x)
@@ -669,7 +666,7 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
           for (int k = 0; k < NA; ++k)
             st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, S + k, q0 + v), c.tag, aff_get(tagg[v], k));
         stress_pause(c, tl.p, tl.chain, 1);
-        lookback<S, V, TW, NSLOT, Op::LB_WINDOW>(c, tl, carry);
+        lookback<S, V, TW, NSLOT>(c, tl, carry);
       } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
@@ -967,7 +964,6 @@ struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = REV, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   struct Args {
     Common c;
     const void* a;
@@ -1059,7 +1055,6 @@ struct NewtonOp {
   static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   struct Args {
     Common c;
     const void* pre[4];
@@ -1469,7 +1464,6 @@ struct VjpOp {
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = true, RESID = false;
   static constexpr int NSLOT = S + S * S + S;
-  static constexpr int LB_WINDOW = S == 1 ? PR_LB_W1 : (S == 2 ? 2 : 1);
   static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
   struct Args {
     Common c;
@@ -1513,37 +1507,15 @@ struct VjpOp {
     // loads first: evaluation e (0..L) is the cell step at t = t_lo + e, which needs U_t and
     // s_{t-1}; e = L belongs to the next lane's first step and only contributes its Jacobian
     float u[G][L + 1][V], sp[S][L + 1][V], gv[L][V];
-    if (!MASKED && a.c.off32) {
-      // full lanes: every address is the wave's uniform base element plus a step offset (scalar) and the
-      // lane's 32-bit offset, so no load needs 64-bit vector address arithmetic; the state before the very
-      // first step is s0 (below), not loaded
 #pragma unroll
-      for (int e = 0; e <= L; ++e) {
-        const int64_t ub = tl.wbase + e * D;
+    for (int e = 0; e <= L; ++e) {
+      const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
+      const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
 #pragma unroll
-        for (int g = 0; g < G; ++g) ldv_u<V, DT>(a.pre[g], ub, tl.loff, u[g][e]);
+      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
 #pragma unroll
-        for (int k = 0; k < S; ++k) {
-          if (e > 0 || tl.t_lo != 0) {
-            ldv_u<V, DT_F32>(a.s + k * N, ub - D, tl.loff, sp[k][e]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < V; ++v) sp[k][e][v] = 0.0f;
-          }
-        }
-        if (e < L) ldv_u<V, DT_F32>(a.g, ub, tl.loff, gv[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e <= L; ++e) {
-        const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
-        const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
-#pragma unroll
-        for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
-        if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
-      }
+      for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
+      if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
     }
     if (tl.t_lo == 0) {
       float x[V][S];
@@ -1649,7 +1621,6 @@ struct VjpOp {
       for (int j = 0; j < NP; ++j) par[v][j] = 0.0f;
     if (tl.active) {
       const int64_t base = (tl.b * T + tl.t_lo) * D + tl.d0;
-      const bool fast = a.c.off32 && tl.nvalid == L;   // every step of the lane exists
 #pragma unroll
       for (int s = 0; s < L; ++s) {
         const int i = L - 1 - s;
@@ -1711,13 +1682,8 @@ struct VjpOp {
           }
         }
         const int64_t idx = base + i * D;
-        if (fast) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) stv_u<V>(a.d_pre + g * N, tl.wbase + i * D, tl.loff, du[g]);
-        } else {
-#pragma unroll
-          for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
-        }
+        for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
         if (a.lambda_out) {
 #pragma unroll
           for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);

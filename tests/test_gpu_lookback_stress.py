@@ -1,10 +1,11 @@
 """Look-back race stress: the library built with -DPR_LB_STRESS=1 (libpararnn_stress.so) pauses tiles for
-pseudo-random times around the publication of their look-back words, so that later tiles find long runs
-of predecessors that have published only their aggregate and walk far back.  Every scan of the method (the
-Newton update's linear solve, the plain linear scan, the adjoint's reverse scan; pararnn-torch README,
-"Method") joins its time chunks this way, and the carry a tile builds must not depend on how far its walk
-went: each result of the stress build must equal the plain library's bit for bit, run after run, while the
-walks really do reach several tiles back.  The first mismatch ends the test (the loops assert as they go).
+pseudo-random times around the publication of their look-back words, so that tiles find their predecessor
+with only its aggregate published and take the other path to their carry (that aggregate applied to the
+state of the tile before it).  Every scan of the method (the Newton update's linear solve, the plain linear
+scan, the adjoint's reverse scan; pararnn-torch README, "Method") joins its time chunks this way, and the
+carry must not depend on which path a tile took: each result of the stress build must equal the plain
+library's bit for bit, run after run, while the aggregate path is really taken.  The first mismatch ends the
+test (the loops assert as they go).
 """
 import numpy as np
 import pytest
@@ -24,7 +25,8 @@ def announce(*a):
 
 def _both(fn):
     """fn() with the plain library, then RUNS times with the stress build: the plain result and the deepest
-    walk the stress runs saw; every stress result is compared with the plain one bit for bit."""
+    walk the stress runs saw (1: some carry came from an aggregate); every stress result is compared with the
+    plain one bit for bit."""
     ref = fn()
     with api.using_library(api.STRESS_LIB_PATH):
         api.lookback_depth(reset=True)
@@ -35,7 +37,7 @@ def _both(fn):
                     continue
                 assert torch.equal(got[k], ref[k]), (k, run)
         depth = api.lookback_depth(reset=True)
-    print("  deepest walk:", depth, "aggregates", flush=True)
+    print("  deepest walk:", depth, "aggregate(s)", flush=True)
     return ref, depth
 
 
@@ -56,7 +58,7 @@ def test_linear_scan_stress(S, reverse, dtype):
         a, b = dev(A), dev(rng.standard_normal((2, B, T, D)).astype(np.float32))
     s0 = dev(synth.random_state(S, B, D, seed=21))
     _, depth = _both(lambda: {"h": api.linear_scan(a, b, s0=s0, reverse=reverse).clone()})
-    assert depth >= 2
+    assert depth >= 1
 
 
 @pytest.mark.parametrize("cell,dtype,fuse", [("gru", "bf16", 1), ("gru", "bf16", 0), ("gru", "f32", 3),
@@ -72,13 +74,13 @@ def test_newton_stress(cell, dtype, fuse):
         h, rep = api.newton_solve(cell, pre, w, b, max_iters=4, s0=s0, fuse_iters=fuse)
         return {"h": h.clone(), "res": torch.tensor(rep.residuals)}
     ref, depth = _both(run)
-    assert depth >= 2
+    assert depth >= 1
 
     def vjp():
         g = api.scan_vjp(cell, pre, ref["h"], dev(inp.g), w, b, s0=s0, want_lambda=True)
         return {k: (None if v is None else v.clone()) for k, v in g.items()}
     _, depth = _both(vjp)
-    assert depth >= 2
+    assert depth >= 1
 
 
 def test_tolerance_mode_and_packed_stress():
@@ -92,4 +94,4 @@ def test_tolerance_mode_and_packed_stress():
         h, rep = api.newton_solve("gru", pre, w, b, max_iters=8, tol=1e-5, cu_seqlens=cu)
         return {"h": h.clone(), "res": torch.tensor(rep.residuals + [rep.iters])}
     _, depth = _both(run)
-    assert depth >= 2
+    assert depth >= 1

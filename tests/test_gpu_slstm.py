@@ -62,6 +62,20 @@ def test_slstm_tolerance_mode_reaches_the_unroll():
     assert max_abs(got.cpu().numpy(), oracle.unroll(prob)) <= 1e-4
 
 
+def test_slstm_tolerance_count_equals_the_oracle_on_the_whole_problem():
+    # the README's sLSTM benchmark shape (B = 8, D = 256) at T = 1024: 8 Picard sweeps, then Newton to 1e-5.
+    # The count is set by the slowest of the 2048 channels, so it is compared with the fp64 oracle on every
+    # channel (a sample of channels converges sooner), and so is the iterate
+    inp = synth.make_inputs("slstm", 8, 1024, 256, seed=4001)
+    prob = oracle_problem(inp)
+    H, ores, oit, oconv, _ = oracle.newton(prob, 40, tol=1e-5, picard=8)
+    got, rep = api.newton_solve("slstm", dev_pre(inp), dev(inp.w), dev(inp.bias), max_iters=40, tol=1e-5,
+                                picard_iters=8)
+    print("  gpu iters", rep.iters, rep.residuals[8:], "oracle iters", oit, list(ores[8:]))
+    assert rep.converged and oconv and rep.iters == oit
+    assert rel_err(got.cpu().numpy(), H) <= 1e-4
+
+
 @pytest.mark.parametrize("dtype,shape", [("f32", (2, 700, 40)), ("bf16", (1, 1200, 16)), ("f32", (1, 65, 2))])
 def test_slstm_vjp(dtype, shape):
     B, T, D = shape
