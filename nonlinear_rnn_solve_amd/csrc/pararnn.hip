@@ -399,41 +399,54 @@ template <int S, int V, int TW, int NSLOT>
 DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
   const int64_t p1 = tl.p - 1, p2 = tl.p - 2;
+  const int q0 = tl.qlane * V;
   bool have_agg = false;   // p-1's aggregate is out (then agg holds it)
   Aff<S> agg[V];
-#if PR_LB_STRESS
-  uint32_t depth = 0;
-#endif
+  uint32_t depth = 0;      // 1 once the carry came from an aggregate (counted in stress builds)
   while (true) {
-    uint64_t wi[V][S];
+    // a scalar state requests every word a round may use before looking at any (one memory round trip);
+    // larger states request p-1's inclusive word, then its aggregate, then p-2's inclusive word, each only
+    // while still needed (fewer words live at once: the 2x2 and 4x4 kernels are short of registers)
+    uint64_t w1[V][S], wa[V][NA], w2[V][S];
+    const bool want_a = !have_agg && p2 >= 0, want_2 = p2 >= 0 && (S == 1 || have_agg);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int k = 0; k < S; ++k) w1[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, k, q0 + v));
+      if (S == 1 && want_a) {
+#pragma unroll
+        for (int k = 0; k < NA; ++k) wa[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, S + k, q0 + v));
+      }
+      if (S == 1 && want_2) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) w2[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p2, tl.chain, k, q0 + v));
+      }
+    }
+    bool ok1 = true;
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
-      for (int k = 0; k < S; ++k) wi[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, k, tl.qlane * V + v));
-    bool inc_ok = true;
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-#pragma unroll
-      for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[v][k], c.tag);
-    if (inc_ok) {
+      for (int k = 0; k < S; ++k) ok1 = ok1 && word_ok(w1[v][k], c.tag);
+    if (ok1) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < S; ++k) carry[v][k] = word_val(wi[v][k]);
+        for (int k = 0; k < S; ++k) carry[v][k] = word_val(w1[v][k]);
       break;
     }
-    if (!have_agg && p2 >= 0) {
-      uint64_t wa[V][NA];
+    if (want_a) {
+      if constexpr (S > 1) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < NA; ++k) wa[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, S + k, q0 + v));
+      }
+      bool oka = true;
 #pragma unroll
       for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < NA; ++k) wa[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p1, tl.chain, S + k, tl.qlane * V + v));
-      bool agg_ok = true;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[v][k], c.tag);
-      if (agg_ok) {
+        for (int k = 0; k < NA; ++k) oka = oka && word_ok(wa[v][k], c.tag);
+      if (oka) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
@@ -441,12 +454,13 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
         have_agg = true;
       }
     }
-    if (have_agg) {
-      uint64_t w2[V][S];
+    if (have_agg && (S > 1 || want_2)) {
+      if constexpr (S > 1) {
 #pragma unroll
-      for (int v = 0; v < V; ++v)
+        for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int k = 0; k < S; ++k) w2[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p2, tl.chain, k, tl.qlane * V + v));
+          for (int k = 0; k < S; ++k) w2[v][k] = ld_word(word_at<S, TW, NSLOT>(c, p2, tl.chain, k, q0 + v));
+      }
       bool ok2 = true;
 #pragma unroll
       for (int v = 0; v < V; ++v)
@@ -462,9 +476,7 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
 #pragma unroll
           for (int k = 0; k < S; ++k) carry[v][k] = x[k];
         }
-#if PR_LB_STRESS
         depth = 1;
-#endif
         break;
       }
     }
@@ -472,6 +484,8 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   }
 #if PR_LB_STRESS
   atomicMax(&g_lb_max_depth, depth);
+#else
+  (void)depth;
 #endif
 }
 
