@@ -13,10 +13,12 @@
 extern "C" {
 #endif
 
-/* The deepest look-back walk since the last reset: 0 when every tile took its carry from its predecessor's
- * inclusive word, 1 once some tile took it from its predecessor's aggregate applied to the inclusive word
- * before that (the walk never goes deeper).  Waits for the device; reset != 0 clears the counter after
- * reading it.  Returns the depth (>= 0) or PARARNN_ERR_HIP (-4) when a HIP call fails. */
+/* The deepest look-back walk since the last reset: the most aggregates any tile passed before it met an
+ * inclusive word.  0 when every tile took its carry from its predecessor's inclusive word; 1 once some tile
+ * took it from its predecessor's aggregate applied to the inclusive word before that (the deepest the
+ * scalar and 2x2 kernels and every VJP go); the sLSTM Newton iteration walks on past as many aggregates as
+ * are out.  Waits for the device; reset != 0 clears the counter after reading it.  Returns the depth (>= 0)
+ * or PARARNN_ERR_HIP (-4) when a HIP call fails. */
 int pararnn_debug_lookback_depth(int reset);
 
 #ifdef __cplusplus

@@ -396,7 +396,7 @@ DEV void stress_pause(const Common& c, int64_t p, int chain, uint32_t site) {
 // tickets (running or done), and position 0 publishes its inclusive word without waiting.  All V channels
 // of the lane wait together: their words were written together by one lane of the predecessor.
 template <int S, int V, int TW, int NSLOT>
-DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
+DEV void lookback_near(const Common& c, const Tile& tl, float (&carry)[V][S]) {
   constexpr int NA = S * S + S;
   const int64_t p1 = tl.p - 1, p2 = tl.p - 2;
   const int q0 = tl.qlane * V;
@@ -487,6 +487,69 @@ DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
 #else
   (void)depth;
 #endif
+}
+
+// The same carry by a walk: each round reads one position's inclusive and aggregate words together,
+// starting at p-1; past a position whose aggregate alone is out it moves one back, until it meets an
+// inclusive word.  That state is then advanced through the passed aggregates one at a time in scan order
+// (re-read: a word never changes once tagged), which is again the chain each tile publishes, bit for
+// bit, however deep the walk went.  Nothing is held from one round to the next.
+template <int S, int V, int TW, int NSLOT>
+DEV void lookback_walk(const Common& c, const Tile& tl, float (&carry)[V][S]) {
+  constexpr int NA = S * S + S;
+  const int q0 = tl.qlane * V;
+  int64_t m = tl.p - 1;   // the position this round looks at
+  while (true) {
+    uint64_t wi[V][S], wa[V][NA];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int k = 0; k < S; ++k) wi[v][k] = ld_word(word_at<S, TW, NSLOT>(c, m, tl.chain, k, q0 + v));
+#pragma unroll
+      for (int k = 0; k < NA; ++k) wa[v][k] = ld_word(word_at<S, TW, NSLOT>(c, m, tl.chain, S + k, q0 + v));
+    }
+    bool inc_ok = true, agg_ok = true;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int k = 0; k < S; ++k) inc_ok = inc_ok && word_ok(wi[v][k], c.tag);
+#pragma unroll
+      for (int k = 0; k < NA; ++k) agg_ok = agg_ok && word_ok(wa[v][k], c.tag);
+    }
+    if (inc_ok) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float x[S];
+#pragma unroll
+        for (int k = 0; k < S; ++k) x[k] = word_val(wi[v][k]);
+        // the aggregates of positions m+1 .. p-1, passed on the way, re-read and applied in scan order
+        for (int64_t pos = m + 1; pos < tl.p; ++pos) {
+          Aff<S> e;
+#pragma unroll
+          for (int k = 0; k < NA; ++k)
+            aff_set(e, k, word_val(ld_word(word_at<S, TW, NSLOT>(c, pos, tl.chain, S + k, q0 + v))));
+          apply(e, x);
+        }
+#pragma unroll
+        for (int k = 0; k < S; ++k) carry[v][k] = x[k];
+      }
+#if PR_LB_STRESS
+      atomicMax(&g_lb_max_depth, static_cast<uint32_t>(tl.p - 1 - m));
+#endif
+      return;
+    }
+    if (agg_ok) --m;   // pass m (position 0 publishes its inclusive word at once: m stays >= 0)
+    else __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// the carry of a tile: the walk for the kernels it leaves with fewer registers (the sLSTM Newton
+// iteration: 253 VGPRs, two waves per SIMD, against 264 and one wave with lookback_near), else the wait
+// at most one aggregate deep
+template <int S, int V, int TW, int NSLOT, bool WALK>
+DEV void lookback(const Common& c, const Tile& tl, float (&carry)[V][S]) {
+  if constexpr (WALK) lookback_walk<S, V, TW, NSLOT>(c, tl, carry);
+  else lookback_near<S, V, TW, NSLOT>(c, tl, carry);
 }
 
 // max(x, x of another lane) over a DPP lane pattern; rows outside ROWS read 0 (keep x)
@@ -680,7 +743,7 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
           for (int k = 0; k < NA; ++k)
             st_word(word_at<S, TW, NSLOT>(c, tl.p, tl.chain, S + k, q0 + v), c.tag, aff_get(tagg[v], k));
         stress_pause(c, tl.p, tl.chain, 1);
-        lookback<S, V, TW, NSLOT>(c, tl, carry);
+        lookback<S, V, TW, NSLOT, Op::LB_WALK>(c, tl, carry);
       } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
@@ -976,7 +1039,7 @@ DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&
 template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
-  static constexpr bool REVERSE = REV, RESID = false;
+  static constexpr bool REVERSE = REV, RESID = false, LB_WALK = false;
   static constexpr int NSLOT = S + S * S + S;
   struct Args {
     Common c;
@@ -1066,6 +1129,7 @@ struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
   static constexpr bool REVERSE = false, RESID = true;
+  static constexpr bool LB_WALK = CELL == CELL_SLSTM;   // see lookback
   static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
   static constexpr int NSLOT = HALO + S;
@@ -1476,7 +1540,7 @@ template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SE
 struct VjpOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
-  static constexpr bool REVERSE = true, RESID = false;
+  static constexpr bool REVERSE = true, RESID = false, LB_WALK = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
   struct Args {

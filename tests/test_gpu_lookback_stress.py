@@ -25,7 +25,7 @@ def announce(*a):
 
 def _both(fn):
     """fn() with the plain library, then RUNS times with the stress build: the plain result and the deepest
-    walk the stress runs saw (1: some carry came from an aggregate); every stress result is compared with the
+    walk the stress runs saw (>= 1: some carry came from an aggregate); every stress result is compared with the
     plain one bit for bit."""
     ref = fn()
     with api.using_library(api.STRESS_LIB_PATH):
@@ -78,6 +78,30 @@ def test_newton_stress(cell, dtype, fuse):
 
     def vjp():
         g = api.scan_vjp(cell, pre, ref["h"], dev(inp.g), w, b, s0=s0, want_lambda=True)
+        return {k: (None if v is None else v.clone()) for k, v in g.items()}
+    _, depth = _both(vjp)
+    assert depth >= 1
+
+
+def test_slstm_newton_walk_stress():
+    """The sLSTM Newton iteration takes its carry by the walk (any depth, the passed aggregates re-read and
+    applied in order); its VJP by the wait at most one aggregate deep."""
+    announce("slstm newton + vjp stress")
+    B, T, D = 1, 32768, 64
+    inp = synth.make_inputs("slstm", B, T, D, dtype="f32", seed=2400, with_grad=True)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    s0 = synth.random_state(4, B, D, seed=24)
+    s0[1] = np.abs(s0[1]) + 0.5     # the normaliser n is positive
+    s0 = dev(s0)
+
+    def run():
+        h, rep = api.newton_solve("slstm", pre, w, b, max_iters=6, picard_iters=2, s0=s0)
+        return {"h": h.clone(), "res": torch.tensor(rep.residuals)}
+    ref, depth = _both(run)
+    assert depth >= 2     # the walk passed several aggregates and re-read them
+
+    def vjp():
+        g = api.scan_vjp("slstm", pre, ref["h"], dev(inp.g), w, b, s0=s0, want_lambda=True)
         return {k: (None if v is None else v.clone()) for k, v in g.items()}
     _, depth = _both(vjp)
     assert depth >= 1
