@@ -2056,12 +2056,18 @@ __global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce1(const flo
   const int64_t per = (R + kRedSlices - 1) / kRedSlices;
   const int64_t r0 = blockIdx.y * per, r1 = r0 + per < R ? r0 + per : R;
   float sum = 0.0f;
-  if (o < n_out) {
+  if (o < n_out && r0 + rg < r1) {
     const int j = static_cast<int>(o / D);
     const int64_t d = o - j * D;
+    // row r = b * n_chunks + ch, stepped kRedRows at a time without a division per row
+    int64_t b = (r0 + rg) / n_chunks, ch = r0 + rg - b * n_chunks;
     for (int64_t r = r0 + rg; r < r1; r += kRedRows) {
-      const int64_t b = r / n_chunks, ch = r - b * n_chunks;
       sum += partial[(ch * npar + j) * C + b * D + d];
+      ch += kRedRows;
+      while (ch >= n_chunks) {
+        ch -= n_chunks;
+        ++b;
+      }
     }
   }
   sh[rg][col] = sum;
