@@ -104,10 +104,9 @@ def source_hash() -> str:
     return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
 
 
-def measured_traffic(key: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary
-    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same
-    counter reads for a copy of known size), or None when that summary was taken on other source."""
+def measured_record(key: str):
+    """The committed counter summary of a workload's dominant kernel (profiles/traffic.json), or None when
+    that summary was taken on other source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -116,7 +115,14 @@ def measured_traffic(key: str):
         return None
     if rec.get("source_sha256") != source_hash():
         return None
-    k = rec.get("kernels", {}).get(key)
+    return rec.get("kernels", {}).get(key)
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by what the same counter reads for a copy of known size), or None
+    when that summary was taken on other source."""
+    k = measured_record(key)
     return None if k is None else float(k["bytes_per_launch"])
 
 
@@ -266,9 +272,14 @@ def main():
                                            % (iters, iteration_bytes(wl.cell, wl.dtype, True),
                                               iteration_bytes(wl.cell, wl.dtype, False)),
                     "algorithmic_bytes": per_elem * N, "kernel_ms": kern_ms,
+                    "frac_note": "effective: the method's bytes for one HBM pass per iteration over the solve's "
+                                 "time; the fused pass reads the gate inputs once for all its iterations and keeps "
+                                 "the trajectory on chip, so a value above 1 is the margin over that bound, and the "
+                                 "pass is bound by vector ALU issue instead (alu, valu_busy)",
                     "alu": {"achieved": tflops, "peak": VALU_FP32_NONPACKED_TFLOPS, "unit": "TFLOP/s",
                             "frac": tflops / VALU_FP32_NONPACKED_TFLOPS,
-                            "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops},
+                            "flops_per_elem_iter": FLOPS_PER_ELEM_ITER[wl.cell], "algorithmic_flops": flops,
+                            "issue": (measured_record(wl.name) or {}).get("issue")},
                     "copy_gbs": copy_gbs(torch, dev)}
     line = {
         "metric": METRIC, "value": value, "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
