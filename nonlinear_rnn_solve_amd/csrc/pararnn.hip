@@ -795,6 +795,24 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
   }
 }
 
+// The residual part of tile_scan alone, for a launch whose elements all have A = 0 (a Picard sweep: every
+// state is its own element's b, so no scan and no look-back are needed): the tile's max of the lanes' rmax
+// goes to res_slot.  Every thread of the workgroup calls it (one barrier inside).
+template <class Op>
+DEV void tile_resid(uint32_t* res_slot, const Tile& tl, float rmax, const TileShm<Op>& sh) {
+  constexpr int NW = Op::NW;
+  auto& sh_red = sh.red;
+  rmax = wave_nanmax(rmax);
+  if (tl.lane == 0) sh_red[tl.wave] = rmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = max(m, __float_as_uint(sh_red[w]));
+    atomicMax(res_slot, m);
+  }
+}
+
 template <class Op>
 DEV uint32_t* op_res_slot(const typename Op::Args& a) {
   if constexpr (Op::RESID) return a.res_slot;
@@ -827,7 +845,17 @@ void k_tile(const typename Op::Args a) {
     typename Op::Lane ln;
     const float rmax = Op::produce(a, tl, ln);
     float x[V][S];
-    tile_scan<Op>(a, c, op_res_slot<Op>(a), tl, ln, rmax, sh, x);
+    if (Op::pointwise(a)) {   // uniform
+      // each element is (0, f): the state entering a lane only ever meets a zero A, and apply gives f for
+      // any finite state, exactly as the scan would
+      tile_resid<Op>(op_res_slot<Op>(a), tl, rmax, sh);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < S; ++k) x[v][k] = 0.0f;
+    } else {
+      tile_scan<Op>(a, c, op_res_slot<Op>(a), tl, ln, rmax, sh, x);
+    }
     Op::finish(a, tl, ln, x);
     if constexpr (!LOOP) return;
     __syncthreads();   // the tile's shared memory and ticket are free again
@@ -1065,6 +1093,7 @@ struct LinearOp {
     Aff<S> e[V][L];
   };
   static DEV bool skip(const Args&) { return false; }
+  static DEV bool pointwise(const Args&) { return false; }
   static constexpr uint32_t EMASK = kFullMask<S>;
   static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args& a, const Tile& tl, float (&x)[V][S]) {
@@ -1163,6 +1192,7 @@ struct NewtonOp {
   struct Lane {
     Aff<S> e[V][L];
   };
+  static DEV bool pointwise(const Args& a) { return a.picard != 0; }   // a Picard sweep: elements (0, f)
   static DEV bool skip(const Args& a) {
     if (!(a.tol > 0.0f)) return false;
     for (int j = 0; j < a.k; ++j) {
@@ -1576,6 +1606,7 @@ struct VjpOp {
     float ac[V];          // GRU: a_c, for d h'/d u_r
   };
   static DEV bool skip(const Args&) { return false; }
+  static DEV bool pointwise(const Args&) { return false; }
   static constexpr uint32_t EMASK = CELL == CELL_SLSTM ? kSlstmJtMask : kFullMask<S>;   // elements are J_{t+1}^T
   static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
