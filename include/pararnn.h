@@ -15,8 +15,10 @@
  *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
- *    memory; the library never allocates device memory and keeps no state
- *    between calls except a process-wide launch counter.
+ *    memory; the library never allocates device memory (the allocation-free
+ *    entry point's workspace is a static device array) and keeps no state
+ *    between calls except a process-wide launch counter and, per device, the
+ *    number of workgroups of a kernel that fit on it at once (queried once).
  *  - Layouts are dense and row-major: a "[B][T][D]" plane has element
  *    (b, t, d) at offset (b*T + t)*D + d, channels (d) fastest.  A state
  *    trajectory "[S][B][T][D]" holds S such planes (LSTM: plane 0 = c,
@@ -160,7 +162,11 @@ typedef struct {
                               for the stop rule; when the rule met an earlier one, a second launch
                               recomputes the trajectory from the first iterate with the right count
                               (so a solve whose init_guess overlaps s_out uses one launch per
-                              iteration there).  Workspace: one set of look-back words per fused
+                              iteration there), and single launches follow for the iterations past
+                              m.  That second launch and the single launches after the first mostly
+                              find the stop rule met: they run on as many workgroups as the device
+                              holds at once, looping over the tiles, so exiting costs a few
+                              microseconds.  Workspace: one set of look-back words per fused
                               iteration.                                                          */
 } pararnn_newton_opts;
 

@@ -4,8 +4,10 @@ report, for the diagonal GRU and LSTM in fp32 and bf16 storage.  Cases: fixed bu
 the longest fused launch (so a solve takes several fused launches), s0, the warm start, a first iterate
 in a separate buffer and in the output itself, packed sequences, lengths that end inside a lane's steps,
 channel counts that leave lanes of a tile idle, and tolerance mode whose speculative first launch is too
-long (the re-run recomputes it), exact, or too short (single launches follow).  The fused solve is also
-held to the oracle directly, since a solve now runs fused by default."""
+long (the re-run recomputes it), exact, or too short (single launches follow).  The re-run and the single
+launches after the first take tickets in a loop on a grid of what is resident; the tolerance cases make them
+compute (launch lengths 2 and 3 leave iterations to them, 8 runs past the stop), in the masked and packed
+variants too.  The fused solve is also held to the oracle directly, since a solve now runs fused by default."""
 import numpy as np
 import pytest
 import torch
@@ -73,6 +75,8 @@ CASES = [
     ("lstm", "f32", (2, 3000, 64), dict(max_iters=8, tol=1e-5)),
     ("gru", "f32", (1, 2000, 64), dict(max_iters=8, tol=1e-5, guess=True)),
     ("gru", "f32", (1, 2000, 64), dict(max_iters=8, tol=1e-5, guess=True, in_place=True)),
+    ("gru", "bf16", (2, 3000, 64), dict(max_iters=8, tol=1e-5, seqs=True)),
+    ("lstm", "bf16", (2, 2500, 64), dict(max_iters=8, tol=1e-5, seqs=True)),
     ("gru", "f32", (1, 2000, 64), dict(max_iters=8, tol=1e-1)),              # stops after few iterations
     ("gru", "f32", (1, 2000, 64), dict(max_iters=8, tol=1e-30)),             # never stops: the budget
 ]
