@@ -70,11 +70,16 @@ DEV float tanh_(float x) { return fmaf(-2.0f, hw_rcp(1.0f + hw_exp2(2.0f * kLog2
 DEV float nanmax(float m, float x) { return (x > m || x != x) ? x : m; }
 
 // ------------------------------------------------------------------------------------------------
-// vector loads / stores of V consecutive channels.  Streaming data (read or written once per pass) uses
-// non-temporal accesses when PR_NT_LOAD / PR_NT_STORE are set.
+// vector loads / stores of V consecutive channels.  Streaming data (read or written once per pass) is
+// stored non-temporally (PR_NT_STORE); fp32 planes are loaded non-temporally too (PR_NT_F32: a wave's row of
+// them fills whole cache lines), bf16 planes through the cache (PR_NT_BF16 = 0: a time slice's row is half a
+// line, whose other half the neighbouring channel tile reads soon after).
 // ------------------------------------------------------------------------------------------------
-#ifndef PR_NT_LOAD
-#define PR_NT_LOAD 0
+#ifndef PR_NT_F32
+#define PR_NT_F32 1
+#endif
+#ifndef PR_NT_BF16
+#define PR_NT_BF16 0
 #endif
 #ifndef PR_NT_STORE
 #define PR_NT_STORE 1
@@ -83,9 +88,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <typename T>
+template <bool NT, typename T>
 DEV T ld_stream(const T* p) {
-  if constexpr (PR_NT_LOAD) return __builtin_nontemporal_load(p);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
 }
 template <typename T>
@@ -97,25 +102,26 @@ DEV void st_stream(T* p, T v) {
 template <int V, int DT>
 DEV void ldv(const void* base, int64_t idx, float (&o)[V]) {
   if constexpr (DT == DT_F32) {
+    constexpr bool NT = PR_NT_F32;
     const float* p = static_cast<const float*>(base) + idx;
     if constexpr (V == 1) {
-      o[0] = ld_stream(p);
+      o[0] = ld_stream<NT>(p);
     } else if constexpr (V == 2) {
-      const f32x2 t = ld_stream(reinterpret_cast<const f32x2*>(p));
+      const f32x2 t = ld_stream<NT>(reinterpret_cast<const f32x2*>(p));
       o[0] = t.x; o[1] = t.y;
     } else {
-      const f32x4 t = ld_stream(reinterpret_cast<const f32x4*>(p));
+      const f32x4 t = ld_stream<NT>(reinterpret_cast<const f32x4*>(p));
       o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
     }
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
     if constexpr (V == 1) {
-      o[0] = __uint_as_float(static_cast<uint32_t>(ld_stream(p)) << 16);
+      o[0] = __uint_as_float(static_cast<uint32_t>(ld_stream<PR_NT_BF16>(p)) << 16);
     } else if constexpr (V == 2) {
-      const uint32_t t = ld_stream(reinterpret_cast<const uint32_t*>(p));
+      const uint32_t t = ld_stream<PR_NT_BF16>(reinterpret_cast<const uint32_t*>(p));
       o[0] = __uint_as_float(t << 16); o[1] = __uint_as_float(t & 0xffff0000u);
     } else {
-      const u32x2 t = ld_stream(reinterpret_cast<const u32x2*>(p));
+      const u32x2 t = ld_stream<PR_NT_BF16>(reinterpret_cast<const u32x2*>(p));
       o[0] = __uint_as_float(t.x << 16); o[1] = __uint_as_float(t.x & 0xffff0000u);
       o[2] = __uint_as_float(t.y << 16); o[3] = __uint_as_float(t.y & 0xffff0000u);
     }
@@ -162,25 +168,26 @@ DEV Rsrc rsrc_at(const void* base) {
 }
 template <int V, int DT>
 DEV void ldv_buf(Rsrc r, uint32_t voff, uint32_t soff, float (&o)[V]) {
+  constexpr int AUX = (DT == DT_F32 ? PR_NT_F32 : PR_NT_BF16) ? 2 : 0;   // cache policy 2: non-temporal
   if constexpr (DT == DT_F32) {
     if constexpr (V == 1) {
-      o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+      o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
     } else if constexpr (V == 2) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
       o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
     } else {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
       o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
       o[2] = __uint_as_float(t[2]); o[3] = __uint_as_float(t[3]);
     }
   } else {
     if constexpr (V == 1) {
-      o[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+      o[0] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX)) << 16);
     } else if constexpr (V == 2) {
-      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
       o[0] = __uint_as_float(t << 16); o[1] = __uint_as_float(t & 0xffff0000u);
     } else {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
       o[0] = __uint_as_float(t[0] << 16); o[1] = __uint_as_float(t[0] & 0xffff0000u);
       o[2] = __uint_as_float(t[1] << 16); o[3] = __uint_as_float(t[1] & 0xffff0000u);
     }
