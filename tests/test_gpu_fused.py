@@ -138,3 +138,17 @@ def test_fused_solve_against_the_oracle(cell, dtype, shape, K):
     assert rep.iters == K
     assert err <= (1e-5 if dtype == "f32" else 2e-2) and err <= 1e-4
     np.testing.assert_allclose(rep.residuals, res, rtol=1e-3, atol=1e-5)
+
+
+@pytest.mark.parametrize("cell,dtype,shape", [("gru", "bf16", (1, 65536, 512)), ("lstm", "f32", (2, 16384, 256))])
+def test_looping_launches_with_several_tiles_per_workgroup(cell, dtype, shape):
+    # thousands of tiles against ~1000 resident workgroups: the looping re-run (speculation too long) and the
+    # looping single launches (too short) each take several tiles per workgroup, in ticket order
+    inp, kw = _inputs(cell, dtype, shape, seed=4500 + shape[1])
+    ref = _solve(cell, inp, kw, 1, max_iters=8, tol=1e-5)
+    n = ref[1].iters
+    announce("looping launches", cell, dtype, shape, "needs", n)
+    assert ref[1].converged and 4 <= n <= 7
+    for fuse in (2, api.MAX_FUSE):
+        got = _solve(cell, inp, kw, fuse, max_iters=8, tol=1e-5)
+        assert _same(got, ref), (fuse, float((got[0] - ref[0]).abs().max()), got[1], ref[1])
