@@ -2275,7 +2275,7 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t 
 #define PR_VJP_GRU_CFG 1, 8, 16, 4, 1
 #endif
 #ifndef PR_SLSTM_CFG
-#define PR_SLSTM_CFG 1, 8, 4, 1, 2
+#define PR_SLSTM_CFG 1, 8, 4, 2, 2
 #endif
 #ifndef PR_VJP_SLSTM_CFG
 #define PR_VJP_SLSTM_CFG 1, 4, 4, 1, 4
