@@ -1052,15 +1052,12 @@ DEV SlstmPart slstm_eval(const Params<G, V>& pm, int v, float Uz, float Ui, floa
   return p;
 }
 
-// running max of |r| that is cheap per step; a NaN or an infinity is caught by bad = fma(r, 0, bad)
-// (NaN iff some r was NaN or infinite), and folded into the result at the end
+// running max of |r| by the NaN-propagating maximum (gfx950's v_maximum3_f32 takes two steps' |r| per
+// instruction); the result is NaN iff some r was NaN or infinite
 struct ResidMax {
-  float m = 0.0f, bad = 0.0f;
-  DEV void add(float r) {
-    m = __builtin_fmaxf(m, fabsf(r));
-    bad = fmaf(r, 0.0f, bad);
-  }
-  DEV float get() const { return bad == bad ? m : __builtin_nanf(""); }
+  float m = 0.0f;
+  DEV void add(float r) { m = __builtin_elementwise_maximum(m, fabsf(r)); }
+  DEV float get() const { return m <= 3.40282347e+38f ? m : __builtin_nanf(""); }
 };
 
 template <int S, int V>
