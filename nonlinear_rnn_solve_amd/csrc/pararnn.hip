@@ -1631,15 +1631,47 @@ struct VjpOp {
     // loads first: evaluation e (0..L) is the cell step at t = t_lo + e, which needs U_t and
     // s_{t-1}; e = L belongs to the next lane's first step and only contributes its Jacobian
     float u[G][L + 1][V], sp[S][L + 1][V], gv[L][V];
+    if (!MASKED && a.c.off32 && CELL != CELL_SLSTM) {   // uniform
+      // as NewtonOp::load: one buffer descriptor per plane at the wave's base element, the lane's 32-bit
+      // offset, and the step's row offset as a uniform operand (no vector address arithmetic per load).
+      // s_{t-1} comes from a descriptor one row before the base; its first row only where t_lo > 0 (the
+      // lane at t = 0 takes s0 below, and its row would lie before the plane).  (The sLSTM's 16-channel
+      // rows ran no faster this way, nor the linear scan's loads.)
+      constexpr uint32_t ESZ = DT == DT_F32 ? 4u : 2u;
+      const uint32_t row_u = static_cast<uint32_t>(D) * ESZ, row_f = static_cast<uint32_t>(D) * 4u;
+      const uint32_t vu = tl.loff * ESZ, vf = tl.loff * 4u;
 #pragma unroll
-    for (int e = 0; e <= L; ++e) {
-      const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
-      const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+      for (int g = 0; g < G; ++g) {
+        const Rsrc r = rsrc_at(static_cast<const char*>(a.pre[g]) + tl.wbase * ESZ);
 #pragma unroll
-      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
+        for (int e = 0; e <= L; ++e) ldv_buf<V, DT>(r, vu, e * row_u, u[g][e]);
+      }
 #pragma unroll
-      for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
-      if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
+      for (int k = 0; k < S; ++k) {
+        const Rsrc r = rsrc_at(a.s + (k * N + tl.wbase - D));
+#pragma unroll
+        for (int e = 1; e <= L; ++e) ldv_buf<V, DT_F32>(r, vf, e * row_f, sp[k][e]);
+        if (tl.t_lo > 0) {
+          ldv_buf<V, DT_F32>(r, vf, 0u, sp[k][0]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) sp[k][0][v] = 0.0f;
+        }
+      }
+      const Rsrc rg = rsrc_at(a.g + tl.wbase);
+#pragma unroll
+      for (int e = 0; e < L; ++e) ldv_buf<V, DT_F32>(rg, vf, e * row_f, gv[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e <= L; ++e) {
+        const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
+        const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, u[g][e]);
+#pragma unroll
+        for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, sp[k][e]);
+        if (e < L) ldv<V, DT_F32>(a.g, idx, gv[e]);
+      }
     }
     if (tl.t_lo == 0) {
       float x[V][S];
@@ -1805,12 +1837,22 @@ struct VjpOp {
             }
           }
         }
-        const int64_t idx = base + i * D;
+        if (a.c.off32 && CELL != CELL_SLSTM) {   // uniform: the plane's base element plus the lane's 32-bit offset
+          const int64_t ub = tl.wbase + i * D;
 #pragma unroll
-        for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
-        if (a.lambda_out) {
+          for (int g = 0; g < G; ++g) stv_u<V>(a.d_pre, g * N + ub, tl.loff, du[g]);
+          if (a.lambda_out) {
 #pragma unroll
-          for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);
+            for (int k = 0; k < S; ++k) stv_u<V>(a.lambda_out, k * N + ub, tl.loff, lam[k]);
+          }
+        } else {
+          const int64_t idx = base + i * D;
+#pragma unroll
+          for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
+          if (a.lambda_out) {
+#pragma unroll
+            for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);
+          }
         }
       }
     }
