@@ -2122,7 +2122,7 @@ __global__ void k_segmask(const int32_t* cu, int64_t n, int64_t T, uint32_t* mas
 // reproducible): stage 1 splits the B*n_chunks rows into kRedSlices contiguous slices and sums each
 // slice per output (rows in ascending order within kRedRows interleaved groups, the groups in order);
 // stage 2 sums the slices in order and writes d_w / d_bias.
-constexpr int kRedCols = 64, kRedRows = 4, kRedSlices = 32;
+constexpr int kRedCols = 64, kRedRows = 4, kRedSlices = 32, kRedUnroll = 8;
 __global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce1(const float* partial, int64_t n_chunks,
                                                                       int npar, int64_t B, int64_t D,
                                                                       float* slices) {
@@ -2136,15 +2136,23 @@ __global__ __launch_bounds__(kRedCols * kRedRows) void k_param_reduce1(const flo
   if (o < n_out && r0 + rg < r1) {
     const int j = static_cast<int>(o / D);
     const int64_t d = o - j * D;
-    // row r = b * n_chunks + ch, stepped kRedRows at a time without a division per row
+    // row r = b * n_chunks + ch, stepped kRedRows at a time without a division per row; kRedUnroll rows'
+    // loads are issued before their sums (which still run in row order)
     int64_t b = (r0 + rg) / n_chunks, ch = r0 + rg - b * n_chunks;
-    for (int64_t r = r0 + rg; r < r1; r += kRedRows) {
-      sum += partial[(ch * npar + j) * C + b * D + d];
-      ch += kRedRows;
-      while (ch >= n_chunks) {
-        ch -= n_chunks;
-        ++b;
+    for (int64_t r = r0 + rg; r < r1; r += kRedRows * kRedUnroll) {
+      float v[kRedUnroll];
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u) {
+        v[u] = r + u * kRedRows < r1 ? partial[(ch * npar + j) * C + b * D + d] : 0.0f;
+        ch += kRedRows;
+        while (ch >= n_chunks) {
+          ch -= n_chunks;
+          ++b;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u)
+        if (r + u * kRedRows < r1) sum += v[u];
     }
   }
   sh[rg][col] = sum;
