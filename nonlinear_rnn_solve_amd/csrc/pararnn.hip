@@ -4,7 +4,7 @@
 // abstract on the HF paper list): the trajectory H of a nonlinear recurrence
 // h_t = f(h_{t-1}, x_t) is the unknown of F(H)_t = h_t - f(h_{t-1}, x_t) = 0;
 // Newton iterations solve it, and each iteration's linearised system is a
-// first-order linear recurrence solved by an associative scan over time.  The
+// first-order linear recurrence solved by a parallel prefix scan along T.  The
 // backward pass is the adjoint: a reverse scan with transposed Jacobians.
 //
 // Design (MI355X first):

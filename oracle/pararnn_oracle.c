@@ -14,7 +14,7 @@
  *  - same page, "Method": the backward pass follows the paper's adjoint
  *    equation (a reverse linear recurrence with transposed Jacobians).
  *  - ParaRNN abstract (HF paper list): Newton iterations combined with
- *    parallel reductions, applied to adaptations of LSTM and GRU.
+ *    parallel reductions; it trains LSTM- and GRU-like cells this way.
  *  - The diagonal GRU cell equations are the benchmark statement that comes
  *    with this code base; the LSTM is the textbook cell without peepholes
  *    whose recurrent weights are diagonal and act on h (a reading: the pages

@@ -5,7 +5,7 @@ residual history R_0 .. R_7 of 8 Newton iterations on the same inputs and, from 
 of tolerance mode (the first k with R_k < tol, plus one) at tol = 1e-4, 1e-5 and 1e-6.
 
 The protocol is the one the pararnn-torch README describes: K*(T) and the warm start in section
-"Method", the long-context campaign (agreement tolerance 1e-4, B = 1) in section "Benchmarks".  Inputs are the seeded synthetic ones of the benchmark workloads (GRU: bf16 gate
+"Method", the long-context campaign (iterates within 1e-4 of the unroll, one batch row) in section "Benchmarks".  Inputs are the seeded synthetic ones of the benchmark workloads (GRU: bf16 gate
 inputs, LSTM: fp32), B = 1, D = 1024.  Everything is computed by the fp64 CPU oracle: the iterates
 by Newton with sequential linear solves, the reference by the sequential unroll.
 
