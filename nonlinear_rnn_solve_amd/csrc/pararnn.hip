@@ -681,9 +681,14 @@ DEV void tile_scan(const typename Op::Args& a, const Common& c, uint32_t* res_sl
   Aff<S> excl[V];                                      // slices of this wave before mine, composed
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    Aff<S> g = ln.e[v][REV ? L - 1 : 0];   // the first element itself: no composition with the identity
+    Aff<S> g;
+    if constexpr (Op::LANE_AGG) {
+      g = ln.agg[v];   // composed by the Op while it produced the elements
+    } else {
+      g = ln.e[v][REV ? L - 1 : 0];   // the first element itself: no composition with the identity
 #pragma unroll
-    for (int s = 1; s < L; ++s) g = Op::compose_elem(ln.e[v][REV ? L - 1 - s : s], g);
+      for (int s = 1; s < L; ++s) g = Op::compose_elem(ln.e[v][REV ? L - 1 - s : s], g);
+    }
     excl[v] = aff_id<S>();
     if constexpr (TS > 1) {
       // inclusive scan over slices (Hillis-Steele on lanes LPR apart), then shift by one slice; with two
@@ -1082,7 +1087,7 @@ DEV void load_s0(const float* s0, int64_t B, int64_t D, const Tile& tl, float (&
 template <int S_, int DT, bool REV, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct LinearOp {
   static constexpr int S = S_, V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
-  static constexpr bool REVERSE = REV, RESID = false, LB_WALK = false;
+  static constexpr bool REVERSE = REV, RESID = false, LB_WALK = false, LANE_AGG = false;
   static constexpr int NSLOT = S + S * S + S;
   struct Args {
     Common c;
@@ -1172,7 +1177,7 @@ template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SE
 struct NewtonOp {
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
-  static constexpr bool REVERSE = false, RESID = true;
+  static constexpr bool REVERSE = false, RESID = true, LANE_AGG = false;
   static constexpr bool LB_WALK = CELL == CELL_SLSTM;   // see lookback
   static constexpr bool FUSABLE = CELL == CELL_GRU || CELL == CELL_LSTM;   // k_fused is built for these
   static constexpr int HALO = S + S * S + S;          // slot of the halo words
@@ -1579,30 +1584,33 @@ template <int CELL> struct VjpStash;
 template <> struct VjpStash<CELL_LINEAR> { float hp; };
 template <> struct VjpStash<CELL_GRU> { float pz, pc, hp, r; };
 template <> struct VjpStash<CELL_LSTM> { float dci, dcf, dcg, dho, kh, hp; };
-template <> struct VjpStash<CELL_SLSTM> { float d[16]; float hp; };
 
+struct VjpArgs {
+  Common c;
+  const void* pre[4];
+  const float* w;
+  const float* bias;
+  const float* s0;
+  const float* s;       // trajectory [S][B][T][D]
+  const float* g;       // [B][T][D]
+  float* d_pre;         // [G][B][T][D]
+  float* lambda_out;    // [S][B][T][D] or NULL
+  float* d_s0;          // [S][B][D] or NULL
+  float* partial;       // [n_chunks][NPAR][C]
+  int64_t B;
+  uint32_t* res_slot;   // unused
+};
+
+// the diagonal cells with a state of one or two (the sLSTM: SlstmVjpOp below)
 template <int CELL, int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
 struct VjpOp {
+  static_assert(CELL != CELL_SLSTM, "the sLSTM VJP is SlstmVjpOp");
   static constexpr int S = CellInfo<CELL>::S, G = CellInfo<CELL>::G;
   static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
-  static constexpr bool REVERSE = true, RESID = false, LB_WALK = false;
+  static constexpr bool REVERSE = true, RESID = false, LB_WALK = false, LANE_AGG = false;
   static constexpr int NSLOT = S + S * S + S;
   static constexpr int NPAR = CELL == CELL_LINEAR ? 0 : 2 * G;  // dw[G], dbias[G] partial sums
-  struct Args {
-    Common c;
-    const void* pre[4];
-    const float* w;
-    const float* bias;
-    const float* s0;
-    const float* s;       // trajectory [S][B][T][D]
-    const float* g;       // [B][T][D]
-    float* d_pre;         // [G][B][T][D]
-    float* lambda_out;    // [S][B][T][D] or NULL
-    float* d_s0;          // [S][B][D] or NULL
-    float* partial;       // [n_chunks][NPAR][C]
-    int64_t B;
-    uint32_t* res_slot;   // unused
-  };
+  using Args = VjpArgs;
   struct Lane {
     Aff<S> e[V][L];
     VjpStash<CELL> st[V][L];
@@ -1611,7 +1619,7 @@ struct VjpOp {
   };
   static DEV bool skip(const Args&) { return false; }
   static DEV bool pointwise(const Args&) { return false; }
-  static constexpr uint32_t EMASK = CELL == CELL_SLSTM ? kSlstmJtMask : kFullMask<S>;   // elements are J_{t+1}^T
+  static constexpr uint32_t EMASK = kFullMask<S>;   // elements are J_{t+1}^T
   static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
   static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
 #pragma unroll
@@ -1631,12 +1639,12 @@ struct VjpOp {
     // loads first: evaluation e (0..L) is the cell step at t = t_lo + e, which needs U_t and
     // s_{t-1}; e = L belongs to the next lane's first step and only contributes its Jacobian
     float u[G][L + 1][V], sp[S][L + 1][V], gv[L][V];
-    if (!MASKED && a.c.off32 && CELL != CELL_SLSTM) {   // uniform
+    if (!MASKED && a.c.off32) {   // uniform
       // as NewtonOp::load: one buffer descriptor per plane at the wave's base element, the lane's 32-bit
       // offset, and the step's row offset as a uniform operand (no vector address arithmetic per load).
       // s_{t-1} comes from a descriptor one row before the base; its first row only where t_lo > 0 (the
-      // lane at t = 0 takes s0 below, and its row would lie before the plane).  (The sLSTM's 16-channel
-      // rows ran no faster this way, nor the linear scan's loads.)
+      // lane at t = 0 takes s0 below, and its row would lie before the plane).  (The linear scan's loads
+      // ran no faster this way.)
       constexpr uint32_t ESZ = DT == DT_F32 ? 4u : 2u;
       const uint32_t row_u = static_cast<uint32_t>(D) * ESZ, row_f = static_cast<uint32_t>(D) * 4u;
       const uint32_t vu = tl.loff * ESZ, vf = tl.loff * 4u;
@@ -1732,15 +1740,6 @@ struct VjpOp {
           J[0] = q.J00; J[1] = q.J01; J[2] = q.J10; J[3] = q.J11;
           st.dci = q.dc_i; st.dcf = q.dc_f; st.dcg = q.dc_g; st.dho = q.dh_o; st.kh = q.kh;
           st.hp = sp[1][e][v];
-        } else {
-          const SlstmPart q = slstm_eval(pm, v, u[0][e][v], u[1][e][v], u[2][e][v], u[3][e][v], sp[0][e][v],
-                                         sp[1][e][v], sp[2][e][v], sp[3][e][v]);
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            J[k] = q.J[k];
-            st.d[k] = q.d[k];
-          }
-          st.hp = sp[3][e][v];
         }
         if (e < L) {
           const bool okl = !MASKED || e < tl.nvalid;
@@ -1815,17 +1814,6 @@ struct VjpOp {
               par[v][g] = fmaf(du[g][v], st.hp, par[v][g]);
               par[v][4 + g] += du[g][v];
             }
-          } else {
-            // dU_g = sum_i lambda_i d s'_i / d u_g; every gate's w multiplies h_{t-1}
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float acc = 0.0f;
-#pragma unroll
-              for (int i2 = 0; i2 < 4; ++i2) acc = fmaf(x[v][i2], st.d[i2 * 4 + g], acc);
-              du[g][v] = acc;
-              par[v][g] = fmaf(acc, st.hp, par[v][g]);
-              par[v][4 + g] += acc;
-            }
           }
           if (t == 0 && a.d_s0) {
 #pragma unroll
@@ -1837,7 +1825,7 @@ struct VjpOp {
             }
           }
         }
-        if (a.c.off32 && CELL != CELL_SLSTM) {   // uniform: the plane's base element plus the lane's 32-bit offset
+        if (a.c.off32) {   // uniform: the plane's base element plus the lane's 32-bit offset
           const int64_t ub = tl.wbase + i * D;
 #pragma unroll
           for (int g = 0; g < G; ++g) stv_u<V>(a.d_pre, g * N + ub, tl.loff, du[g]);
@@ -1871,6 +1859,218 @@ struct VjpOp {
         float sum = 0.0f;
         for (int w = 0; w < NSEG; ++w) sum += sh_par[j][w][q];
         a.partial[(tl.chunk * NPAR + j) * a.c.C + ch] = sum;
+      }
+    }
+  }
+};
+
+// The sLSTM VJP (same elements and epilogue as VjpOp) with the cell evaluated twice instead of kept: a
+// step's element (a 4x4 transposed Jacobian and b) and its 16 gate partials are 37 values, and holding
+// them from the scan to the re-walk limits a lane to 4 steps at two waves per SIMD.  Here a lane keeps
+// only its inputs (4 gate and 4 state values a step, the upstream gradient), composes its elements into
+// its aggregate while it produces them, and evaluates the cell again in the re-walk for the partials and
+// the Jacobian.  That leaves room for 12 steps a lane, which spreads the scan's per-lane work (the slice
+// scan, the waves' aggregates, the look-back) over three times as many steps.
+template <int DT, int V_, int L_, int NW_, int MINW_, int TS_, bool SEG = false>
+struct SlstmVjpOp {
+  static constexpr int S = 4, G = 4;
+  static constexpr int V = V_, L = L_, NW = NW_, MINW = MINW_, TS = TS_;
+  static constexpr bool REVERSE = true, RESID = false, LB_WALK = false, LANE_AGG = true;
+  static constexpr int NSLOT = S + S * S + S;
+  static constexpr int NPAR = 2 * G;                 // dw[G], dbias[G] partial sums
+  static constexpr uint32_t EMASK = kSlstmJtMask;    // elements are J_{t+1}^T
+  using Args = VjpArgs;
+  struct Lane {
+    Aff<S> agg[V];                               // the lane's elements composed in scan order
+    float u[G][L + 1][V], sp[S][L + 1][V];       // U_t and s_{t-1} of steps t_lo .. t_lo + L
+    float gv[L][V];                              // the upstream gradient of steps t_lo .. t_lo + L - 1
+    uint32_t sb;                                 // packed sequences: sequence-start bits of those steps
+  };
+  static DEV bool skip(const Args&) { return false; }
+  static DEV bool pointwise(const Args&) { return false; }
+  static DEV Aff<S> compose_elem(const Aff<S>& e, const Aff<S>& g) { return compose_masked<S, EMASK>(e, g); }
+  static DEV void init_state(const Args&, const Tile&, float (&x)[V][S]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int k = 0; k < S; ++k) x[v][k] = 0.0f;   // nothing flows in from beyond the last step
+  }
+
+  // the element of step e: A = J_{e+1}^T (Jn: zero past the last step or at a sequence start), b = e_h g_e;
+  // the identity where step e is masked
+  static DEV Aff<S> element(const float (&Jn)[S * S], float g, bool okl) {
+    Aff<S> el;
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+#pragma unroll
+      for (int j = 0; j < S; ++j) el.A[i * S + j] = okl ? Jn[j * S + i] : (i == j ? 1.0f : 0.0f);
+#pragma unroll
+    for (int k = 0; k < S; ++k) el.b[k] = 0.0f;
+    el.b[S - 1] = okl ? g : 0.0f;
+    return el;
+  }
+  template <int V2>
+  static DEV SlstmPart eval(const Params<G, V2>& pm, const Lane& ln, int v, int e) {
+    return slstm_eval(pm, v, ln.u[0][e][v], ln.u[1][e][v], ln.u[2][e][v], ln.u[3][e][v], ln.sp[0][e][v],
+                      ln.sp[1][e][v], ln.sp[2][e][v], ln.sp[3][e][v]);
+  }
+  // whether evaluation e (0..L) takes part: steps inside [0, T), and e = L only where the next lane's
+  // first step exists; and whether its Jacobian reaches back (not at a sequence start)
+  template <bool MASKED>
+  static DEV bool ok_at(const Args& a, const Tile& tl, int e) {
+    return !MASKED || e < tl.nvalid || (e == L && tl.t_lo + L < a.c.T);
+  }
+  static DEV bool live_at(const Lane& ln, int e) { return !(SEG && ((ln.sb >> e) & 1u)); }
+
+  static DEV float produce(const Args& a, const Tile& tl, Lane& ln) {
+    if (tl.t_lo + L < a.c.T) produce_t<false>(a, tl, ln);
+    else produce_t<true>(a, tl, ln);
+    return 0.0f;
+  }
+  template <bool MASKED>
+  static DEV void produce_t(const Args& a, const Tile& tl, Lane& ln) {
+    const int64_t D = a.c.D, T = a.c.T, N = a.c.N, row = tl.b * T;
+#pragma unroll
+    for (int e = 0; e <= L; ++e) {
+      const int64_t idx = (row + (MASKED ? clamp_t(tl.t_lo + e, T) : tl.t_lo + e)) * D + tl.d0;
+      const int64_t idp = (row + clamp_t(tl.t_lo + e - 1, T)) * D + tl.d0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) ldv<V, DT>(a.pre[g], idx, ln.u[g][e]);
+#pragma unroll
+      for (int k = 0; k < S; ++k) ldv<V, DT_F32>(a.s, k * N + idp, ln.sp[k][e]);
+      if (e < L) ldv<V, DT_F32>(a.g, idx, ln.gv[e]);
+    }
+    if (tl.t_lo == 0) {
+      float x[V][S];
+      load_s0<S, V>(a.s0, a.B, D, tl, x);
+#pragma unroll
+      for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) ln.sp[k][0][v] = x[v][k];
+    }
+    ln.sb = 0;
+    if constexpr (SEG) {
+      ln.sb = seg_bits(a.c.seg, tl.t_lo, T);
+#pragma unroll
+      for (int e = 0; e <= L; ++e)
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+#pragma unroll
+          for (int v = 0; v < V; ++v) ln.sp[k][e][v] = ((ln.sb >> e) & 1u) ? 0.0f : ln.sp[k][e][v];
+    }
+    Params<G, V> pm;
+    load_params<CELL_SLSTM, G, V>(a.w, a.bias, D, tl.d0, pm);
+    // evaluations e = L .. 0; the element of step e takes the Jacobian of e + 1, and the lane's aggregate
+    // composes them in scan order (step L - 1 first)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float Jn[S * S];
+#pragma unroll
+      for (int e = L; e >= 0; --e) {
+        const SlstmPart q = eval(pm, ln, v, e);
+        if (e < L) {
+          const Aff<S> el = element(Jn, ln.gv[e][v], !MASKED || e < tl.nvalid);
+          ln.agg[v] = e == L - 1 ? el : compose_elem(el, ln.agg[v]);
+        }
+        const bool live = ok_at<MASKED>(a, tl, e) && live_at(ln, e);
+#pragma unroll
+        for (int k = 0; k < S * S; ++k) Jn[k] = live ? q.J[k] : 0.0f;
+      }
+    }
+  }
+
+  static DEV void finish(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S]) {
+    constexpr int TW = (WAVE / TS) * V, NSEG = NW * TS;
+    __shared__ float sh_par[NPAR][NSEG][TW];
+    float par[V][NPAR];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int j = 0; j < NPAR; ++j) par[v][j] = 0.0f;
+    if (tl.active) {
+      if (tl.t_lo + L < a.c.T) walk<false>(a, tl, ln, x, par);
+      else walk<true>(a, tl, ln, x, par);
+    }
+    const int q0 = tl.qlane * V, seg = tl.wave * TS + tl.slice;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int j = 0; j < NPAR; ++j) sh_par[j][seg][q0 + v] = par[v][j];
+    __syncthreads();
+    // fixed-order sum over the waves of the tile
+    for (int idx = threadIdx.x; idx < NPAR * TW; idx += NW * WAVE) {
+      const int j = idx / TW, q = idx % TW;
+      const int64_t ch = static_cast<int64_t>(tl.chain) * TW + q;
+      if (ch >= a.c.C) continue;
+      float sum = 0.0f;
+      for (int w = 0; w < NSEG; ++w) sum += sh_par[j][w][q];
+      a.partial[(tl.chunk * NPAR + j) * a.c.C + ch] = sum;
+    }
+  }
+  // the re-walk from the state entering the lane (lambda after its last step), steps L-1 .. 0: each step's
+  // cell again (its partials, and its Jacobian for the step before), lambda_t, dU_t and the parameter sums
+  template <bool MASKED>
+  static DEV void walk(const Args& a, const Tile& tl, Lane& ln, float (&x)[V][S], float (&par)[V][NPAR]) {
+    const int64_t D = a.c.D, N = a.c.N;
+    const int64_t base = (tl.b * a.c.T + tl.t_lo) * D + tl.d0;
+    Params<G, V> pm;
+    load_params<CELL_SLSTM, G, V>(a.w, a.bias, D, tl.d0, pm);
+    float Jn[V][S * S];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const SlstmPart q = eval(pm, ln, v, L);
+      const bool live = ok_at<MASKED>(a, tl, L) && live_at(ln, L);
+#pragma unroll
+      for (int k = 0; k < S * S; ++k) Jn[v][k] = live ? q.J[k] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < L; ++s) {
+      const int i = L - 1 - s;
+      if (MASKED && i >= tl.nvalid) {   // past T: an identity element, no output; J_i reaches nothing
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int k = 0; k < S * S; ++k) Jn[v][k] = 0.0f;
+        continue;
+      }
+      const int64_t t = tl.t_lo + i;
+      float du[G][V], lam[S][V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const SlstmPart q = eval(pm, ln, v, i);
+        apply_masked<S, EMASK>(element(Jn[v], ln.gv[i][v], true), x[v]);
+#pragma unroll
+        for (int k = 0; k < S; ++k) lam[k][v] = x[v][k];
+        const float hp = ln.sp[3][i][v];
+        // dU_g = sum_i lambda_i d s'_i / d u_g; every gate's w multiplies h_{t-1}
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) acc = fmaf(x[v][i2], q.d[i2 * 4 + g], acc);
+          du[g][v] = acc;
+          par[v][g] = fmaf(acc, hp, par[v][g]);
+          par[v][4 + g] += acc;
+        }
+        if (t == 0 && a.d_s0) {
+#pragma unroll
+          for (int i2 = 0; i2 < S; ++i2) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < S; ++j) acc = fmaf(q.J[j * S + i2], x[v][j], acc);
+            a.d_s0[(i2 * a.B + tl.b) * D + tl.d0 + v] = acc;
+          }
+        }
+        const bool live = live_at(ln, i);
+#pragma unroll
+        for (int k = 0; k < S * S; ++k) Jn[v][k] = live ? q.J[k] : 0.0f;
+      }
+      const int64_t idx = base + i * D;
+#pragma unroll
+      for (int g = 0; g < G; ++g) stv<V>(a.d_pre + g * N + idx, du[g]);
+      if (a.lambda_out) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) stv<V>(a.lambda_out + k * N + idx, lam[k]);
       }
     }
   }
@@ -2325,7 +2525,7 @@ Geo make_geo(int S, int nslot, int V, int L, int NW, int TS, int64_t B, int64_t 
 #define PR_SLSTM_CFG 1, 8, 4, 2, 2
 #endif
 #ifndef PR_VJP_SLSTM_CFG
-#define PR_VJP_SLSTM_CFG 1, 4, 4, 1, 4
+#define PR_VJP_SLSTM_CFG 1, 12, 4, 2, 2
 #endif
 #ifndef PR_VJP_LSTM_CFG
 #define PR_VJP_LSTM_CFG 1, 4, 16, 4, 1
@@ -2340,6 +2540,10 @@ template <> struct ScanCfg<2> : TileCfg<PR_SCAN2_CFG> {};
 template <int CELL> struct VjpCfg : TileCfg<PR_VJP_GRU_CFG> {};
 template <> struct VjpCfg<CELL_LSTM> : TileCfg<PR_VJP_LSTM_CFG> {};
 template <> struct VjpCfg<CELL_SLSTM> : TileCfg<PR_VJP_SLSTM_CFG> {};
+template <int CELL, int DT, class C, bool SEG>
+struct VjpOpOf { using type = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS, SEG>; };
+template <int DT, class C, bool SEG>
+struct VjpOpOf<CELL_SLSTM, DT, C, SEG> { using type = SlstmVjpOp<DT, C::V, C::L, C::NW, C::MINW, C::TS, SEG>; };
 
 Common make_common(void* ws, const Geo& g, int64_t B, int64_t T, int64_t D, int ticket_slot) {
   Common c;
@@ -2651,7 +2855,7 @@ ScanEntry pick_scan(int S, int dt, int rev, bool seg) {
 template <int CELL, int DT, bool SEG>
 struct VjpKernel {
   using C = VjpCfg<CELL>;
-  using Op = VjpOp<CELL, DT, C::V, C::L, C::NW, C::MINW, C::TS, SEG>;
+  using Op = typename VjpOpOf<CELL, DT, C, SEG>::type;
   static Geo geo(const pararnn_problem* pb) {
     return make_geo(Op::S, Op::NSLOT, C::V, C::L, C::NW, C::TS, pb->B, pb->T, pb->D);
   }
