@@ -80,7 +80,8 @@ def test_slstm_tolerance_count_equals_the_oracle_on_the_whole_problem(T):
     assert rel_err(got.cpu().numpy(), H) <= 1e-4
 
 
-@pytest.mark.parametrize("dtype,shape", [("f32", (2, 700, 40)), ("bf16", (1, 1200, 16)), ("f32", (1, 65, 2))])
+@pytest.mark.parametrize("dtype,shape", [("f32", (2, 700, 40)), ("bf16", (1, 1200, 16)), ("f32", (1, 65, 2)),
+                                         ("f32", (3, 1, 6)), ("f32", (1, 97, 34)), ("f32", (2, 193, 64))])
 def test_slstm_vjp(dtype, shape):
     B, T, D = shape
     announce("slstm vjp", dtype, shape)
