@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import dev, dev_pre, max_abs, oracle_problem, sample_channels, take_channels
+from gpu_util import dev, dev_pre, lane_channels, max_abs, oracle_problem, sample_channels, take_channels
 from nonlinear_rnn_solve_amd import api, synth
 
 pytestmark = pytest.mark.gpu
@@ -78,6 +78,29 @@ def test_slstm_tolerance_count_equals_the_oracle_on_the_whole_problem(T):
     print("  gpu iters", rep.iters, rep.residuals[8:], "oracle iters", oit, list(ores[8:]))
     assert rep.converged and oconv and rep.iters == oit
     assert rel_err(got.cpu().numpy(), H) <= 1e-4
+
+
+def test_slstm_full_size_tolerance_solve_and_vjp():
+    # the largest shape the sLSTM benchmark times (B = 8, T = 65536, D = 256), in its launch configuration: the
+    # tolerance-mode solve against the fp64 unroll, and the VJP at the GPU's trajectory against the oracle's
+    # adjoint at that same trajectory, on sampled channels that hold every lane position of a tile
+    B, T, D = 8, 65536, 256
+    announce("slstm full size", (B, T, D))
+    inp = synth.make_inputs("slstm", B, T, D, seed=4000 + T // 1024, with_grad=True)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    got, rep = api.newton_solve("slstm", pre, w, b, max_iters=40, tol=1e-5, picard_iters=8, final_residual=True)
+    print("  iters", rep.iters, "final residual", rep.final_residual)
+    assert rep.converged and rep.final_residual < 1e-4
+    gr = api.scan_vjp("slstm", pre, got, dev(inp.g), w, b, want_lambda=True)
+    ch = lane_channels(B, D, 8, seed=6)
+    prob = oracle_problem(inp, channels=ch)
+    g_s = take_channels(got.cpu().numpy(), ch)
+    e_un = max_abs(g_s, oracle.unroll(prob))
+    ref = oracle.vjp(prob, g_s.astype(np.float64), take_channels(inp.g, ch))
+    e_lam = rel_err(take_channels(gr["lam"].cpu().numpy(), ch), ref["lam"])
+    e_dp = rel_err(take_channels(gr["d_pre"].cpu().numpy(), ch), ref["d_pre"])
+    print("  vs unroll", e_un, "vjp lambda", e_lam, "d_pre", e_dp)
+    assert e_un <= 1e-4 and e_lam <= 1e-4 and e_dp <= 1e-4
 
 
 @pytest.mark.parametrize("dtype,shape", [("f32", (2, 700, 40)), ("bf16", (1, 1200, 16)), ("f32", (1, 65, 2)),
