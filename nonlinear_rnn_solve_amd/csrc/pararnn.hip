@@ -2764,6 +2764,14 @@ struct NewtonKernel {
   }
 };
 
+// Tolerance mode, cells without a fused pass (the sLSTM): the Newton iterations from this many after the
+// Picard sweeps on run on a grid of what is resident, as the launches after a speculative fused pass do.  Once
+// the solve has stopped such a launch exits in a few us, where one workgroup per tile costs up to ~160 us
+// (B=8, T=65536, D=256); while it still works it is ~15% slower (the looping kernel spills).  The sLSTM
+// workloads stop after 8-17 Newton iterations.  The launch shape leaves every result the same bit for bit.
+#ifndef PR_TAIL_FROM
+#define PR_TAIL_FROM 12
+#endif
 struct NewtonEntry {
   size_t (*ws)(const pararnn_problem*, int);
   pararnn_status (*prepare)(const pararnn_problem*, void*, int, hipStream_t);
@@ -2772,7 +2780,8 @@ struct NewtonEntry {
   // NULL for cells without a fused pass
   pararnn_status (*fused)(const pararnn_problem*, const pararnn_newton_opts*, int, int, bool, float*, void*,
                           hipStream_t);
-  // the single launches after the first one that follows a speculative fused pass (NULL with fused)
+  // the single launches that usually find the solve stopped: after the first one that follows a speculative
+  // fused pass, or (cells without a fused pass) late tolerance-mode iterations
   pararnn_status (*iterate_tail)(const pararnn_problem*, const pararnn_newton_opts*, int, float*, void*,
                                  hipStream_t);
 };
@@ -2781,7 +2790,7 @@ template <int CELL, int DT, bool SEG>
 NewtonEntry newton_entry() {
   using K = NewtonKernel<CELL, DT, SEG>;
   if constexpr (K::Op::FUSABLE) return {K::ws, K::prepare, K::iterate, K::final_residual, K::fused, K::iterate_tail};
-  else return {K::ws, K::prepare, K::iterate, K::final_residual, nullptr, nullptr};
+  else return {K::ws, K::prepare, K::iterate, K::final_residual, nullptr, K::iterate_tail};
 }
 
 template <int CELL, int DT>
@@ -3196,7 +3205,9 @@ pararnn_status pararnn_newton_solve(const pararnn_problem* pb, const pararnn_new
   const size_t traj = static_cast<size_t>(state_size(pb->cell)) * problem_N(pb) * sizeof(float);
   if (m <= 1 || (op->tol > 0.0f && op->init_guess && overlap(op->init_guess, s_out, traj))) {
     // one launch per iteration (a speculative pass could not be re-run: s_out overwrites its start)
-    for (int k = 0; k < K && rc == PARARNN_OK; ++k) rc = ne.iterate(pb, op, k, s_out, ws, st);
+    const int tail = (op->tol > 0.0f && !ne.fused && ne.iterate_tail) ? op->picard_iters + PR_TAIL_FROM : K;
+    for (int k = 0; k < K && rc == PARARNN_OK; ++k)
+      rc = k >= tail ? ne.iterate_tail(pb, op, k, s_out, ws, st) : ne.iterate(pb, op, k, s_out, ws, st);
   } else if (op->tol > 0.0f) {
     // speculative pass of m iterations, its re-run if the stop rule met an earlier one, then single
     // launches that exit at once once the stop rule is met.  The re-run and the launches after the first

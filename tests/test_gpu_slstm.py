@@ -103,6 +103,22 @@ def test_slstm_full_size_tolerance_solve_and_vjp():
     assert e_un <= 1e-4 and e_lam <= 1e-4 and e_dp <= 1e-4
 
 
+def test_slstm_tolerance_launches_on_a_resident_grid_give_the_same_bits():
+    # in tolerance mode the late Newton iterations of a cell without a fused pass run on a grid of what is
+    # resident, each workgroup taking several tiles (here 1024 tiles); the trajectory must equal that of the
+    # same number of iterations at a fixed budget (one workgroup per tile) bit for bit.  This input takes 21
+    # updates, so its last one runs on the resident grid while it still works, and the 19 after it find the
+    # solve stopped
+    announce("slstm resident-grid launches", "f32", (8, 4096, 256))
+    inp = synth.make_inputs("slstm", 8, 4096, 256, seed=4004)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    got, rep = api.newton_solve("slstm", pre, w, b, max_iters=40, tol=1e-5, picard_iters=8)
+    assert rep.converged and rep.iters > 20
+    fixed, rep_f = api.newton_solve("slstm", pre, w, b, max_iters=rep.iters, picard_iters=8)
+    assert torch.equal(got, fixed)
+    np.testing.assert_array_equal(rep.residuals, rep_f.residuals[:rep.iters])
+
+
 @pytest.mark.parametrize("dtype,shape", [("f32", (2, 700, 40)), ("bf16", (1, 1200, 16)), ("f32", (1, 65, 2)),
                                          ("f32", (3, 1, 6)), ("f32", (1, 97, 34)), ("f32", (2, 193, 64))])
 def test_slstm_vjp(dtype, shape):
