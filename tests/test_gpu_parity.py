@@ -378,6 +378,28 @@ def test_full_config_newton(idx):
     np.testing.assert_allclose(rep.residuals, res, rtol=1e-3, atol=1e-5)
 
 
+@pytest.mark.parametrize("idx", [2, 3])
+def test_full_size_vjp_at_the_fixed_budget_workloads(idx):
+    # these workloads time no VJP; here the VJP kernels run at their full shapes (GRU with bf16 gate inputs,
+    # LSTM): at the GPU's converged trajectory against the oracle's adjoint at that same trajectory, on sampled
+    # channels that hold every lane position of a tile (the gradient drawn after the workload's other inputs)
+    wl = synth.WORKLOADS[idx]
+    announce("full vjp", wl.name)
+    inp = synth.make_inputs(wl.cell, wl.B, wl.T, wl.D, dtype=wl.dtype, seed=wl.index, with_grad=True)
+    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    got, rep = api.newton_solve(wl.cell, pre, w, b, max_iters=8, tol=1e-5)
+    assert rep.converged
+    gr = api.scan_vjp(wl.cell, pre, got, dev(inp.g), w, b, want_lambda=True)
+    ch = lane_channels(wl.B, wl.D, 8, seed=7)
+    prob = oracle_problem(inp, channels=ch)
+    g_s = take_channels(got.cpu().numpy(), ch)
+    ref = oracle.vjp(prob, g_s.astype(np.float64), take_channels(inp.g, ch))
+    e_lam = rel_err(take_channels(gr["lam"].cpu().numpy(), ch), ref["lam"])
+    e_dp = rel_err(take_channels(gr["d_pre"].cpu().numpy(), ch), ref["d_pre"])
+    print("  iters", rep.iters, "vjp lambda", e_lam, "d_pre", e_dp)
+    assert e_lam <= 1e-4 and e_dp <= 1e-4
+
+
 @pytest.mark.parametrize("idx", [0, 2, 3])
 def test_full_config_after_convergence(idx):
     # the tolerance-mode run of each fixed-budget workload (tol 1e-5, at most 8 iterations): every element
