@@ -378,15 +378,16 @@ def test_full_config_newton(idx):
     np.testing.assert_allclose(rep.residuals, res, rtol=1e-3, atol=1e-5)
 
 
-@pytest.mark.parametrize("idx", [2, 3])
+@pytest.mark.parametrize("idx", [1, 2, 3])
 def test_full_size_vjp_at_the_fixed_budget_workloads(idx):
-    # these workloads time no VJP; here the VJP kernels run at their full shapes (GRU with bf16 gate inputs,
-    # LSTM): at the GPU's converged trajectory against the oracle's adjoint at that same trajectory, on sampled
+    # these workloads time no VJP; here the VJP kernels run at their full shapes (the linear scan's, the GRU's
+    # with bf16 gate inputs, the LSTM's): at the GPU's converged trajectory against the oracle's adjoint at that same trajectory, on sampled
     # channels that hold every lane position of a tile (the gradient drawn after the workload's other inputs)
     wl = synth.WORKLOADS[idx]
     announce("full vjp", wl.name)
     inp = synth.make_inputs(wl.cell, wl.B, wl.T, wl.D, dtype=wl.dtype, seed=wl.index, with_grad=True)
-    pre, w, b = dev_pre(inp), dev(inp.w), dev(inp.bias)
+    pre = dev_pre(inp)
+    w, b = (None, None) if inp.w is None else (dev(inp.w), dev(inp.bias))
     got, rep = api.newton_solve(wl.cell, pre, w, b, max_iters=8, tol=1e-5)
     assert rep.converged
     gr = api.scan_vjp(wl.cell, pre, got, dev(inp.g), w, b, want_lambda=True)
